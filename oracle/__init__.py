@@ -1,0 +1,11 @@
+"""CPU oracle for the W4A16 group-quantised linear layer.
+
+TEST INFRASTRUCTURE: only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import it. The HIP library never calls it.
+"""
+from .awq_oracle import *  # noqa: F401,F403
+from .awq_oracle import (device_layout_doc, device_words, pack_canonical,  # noqa: F401
+                         unpack_canonical, pack_zeros, unpack_zeros, pack_device,
+                         unpack_device, dequant64, dequant16, linear64, linear64_w16,
+                         l1_scale, normalised_error, linear_bruteforce, round_output16,
+                         weight_set_bytes, model_bytes, low_nibble)

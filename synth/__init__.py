@@ -1,0 +1,116 @@
+"""Seeded synthetic inputs for the W4A16 linear layer.
+
+Shared by the tests, the bench and the smoke check. This module only draws
+random numbers and describes workload shapes: it holds none of the layer's
+arithmetic (no packing, no dequantisation, no products), so the HIP path and
+the CPU oracle can both consume its output without sharing method code.
+
+Value distributions follow the workloads the layer is measured on: codes and
+zero points uniform over 0..15, fp16 scales uniform in [0.001, 0.02] (or
+log-uniform in [1e-3, 3e-2]), fp16 activations N(0, 1), optionally with 1% of
+input channels scaled by 20 (outlier channels). Draw order per layer: codes,
+zero points, scales; activations come from their own stream.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+
+def _rng(*tags: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([int(t) for t in tags]))
+
+
+def layer(K: int, N: int, G: int = 128, seed: int = 0, layer_id: int = 0,
+          scales: str = "uniform", lo: float = 0.001, hi: float = 0.02):
+    """Codes q uint8 [K, N], zero points z uint8 [K/G, N], scales s fp16 [K/G, N]."""
+    if K % G:
+        raise ValueError("K must be a multiple of G")
+    rng = _rng(seed, 1, layer_id, K, N, G)
+    q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
+    z = rng.integers(0, 16, size=(K // G, N), dtype=np.uint8)
+    if scales == "uniform":
+        s = rng.uniform(lo, hi, size=(K // G, N))
+    elif scales == "loguniform":
+        s = np.exp(rng.uniform(np.log(lo), np.log(hi), size=(K // G, N)))
+    else:
+        raise ValueError(scales)
+    return q, z, s.astype(np.float16)
+
+
+def activations(M: int, K: int, seed: int = 0, stream: int = 0,
+                outlier_frac: float = 0.0, outlier_gain: float = 20.0):
+    """x fp16 [M, K] ~ N(0, 1); round(outlier_frac*K) input channels (chosen
+    without replacement) are multiplied by outlier_gain before the fp16 cast."""
+    rng = _rng(seed, 2, stream, M, K)
+    x = rng.standard_normal(size=(M, K))
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        cols = rng.choice(K, n_out, replace=False)
+        x[:, cols] *= outlier_gain
+    return x.astype(np.float16)
+
+
+def outlier_channels(K: int, seed: int = 0, stream: int = 0, M: int = 1,
+                     outlier_frac: float = 0.01):
+    """The channel indices ``activations`` scales (same draws, same order)."""
+    rng = _rng(seed, 2, stream, M, K)
+    rng.standard_normal(size=(M, K))
+    n_out = int(round(outlier_frac * K))
+    return np.sort(rng.choice(K, n_out, replace=False)) if n_out else np.zeros(0, int)
+
+
+@dataclass(frozen=True)
+class Shape:
+    name: str
+    K: int
+    N: int
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    shapes: tuple
+    Ms: tuple
+    G: int = 128
+    layers: int = 1
+    scales: str = "uniform"
+    lo: float = 0.001
+    hi: float = 0.02
+    outlier_frac: float = 0.0
+
+
+# Single layer, M=1, K=N=4096, G=128.
+SINGLE_4096 = Workload("single-4096x4096", (Shape("proj", 4096, 4096),), (1,))
+
+# LLaMA-2-7B-shaped decode set: 32 layers of fused QKV, O, fused gate+up, down.
+LLAMA2_7B_DECODE = Workload(
+    "llama2-7b-decode-stack",
+    (Shape("qkv", 4096, 12288), Shape("o", 4096, 4096),
+     Shape("gate_up", 4096, 22016), Shape("down", 11008, 4096)),
+    (1,), layers=32)
+
+# LLaMA-3-8B-shaped batched decode sweep (GQA: 32 q / 8 kv heads of dim 128).
+LLAMA3_8B_SWEEP = Workload(
+    "llama3-8b-decode-sweep",
+    (Shape("qkv", 4096, 6144), Shape("o", 4096, 4096),
+     Shape("gate_up", 4096, 28672), Shape("down", 14336, 4096)),
+    (1, 2, 4, 8, 16, 32), scales="loguniform", lo=1e-3, hi=3e-2)
+
+# LLaMA-2-13B-shaped prefill with 1% outlier input channels.
+LLAMA2_13B_PREFILL = Workload(
+    "llama2-13b-prefill",
+    (Shape("qkv", 5120, 15360), Shape("o", 5120, 5120),
+     Shape("gate_up", 5120, 27648), Shape("down", 13824, 5120)),
+    (512, 2048), outlier_frac=0.01)
+
+# Falcon-180B-shaped stack (232 q heads + 2 x 8 kv heads of dim 64), 80 layers.
+FALCON_180B_STACK = Workload(
+    "falcon-180b-stack",
+    (Shape("qkv", 14848, 15872), Shape("o", 14848, 14848),
+     Shape("up", 14848, 59392), Shape("down", 59392, 14848)),
+    (1, 16), layers=80)
+
+WORKLOADS = (SINGLE_4096, LLAMA2_7B_DECODE, LLAMA3_8B_SWEEP, LLAMA2_13B_PREFILL,
+             FALCON_180B_STACK)
