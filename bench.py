@@ -1,0 +1,395 @@
+#!/usr/bin/env python3
+"""Benchmark of the W4A16 group-quantised linear layer on one MI355X.
+
+Headline (one JSON line on stdout): weight GB/s of the decode path at M=1 over
+a LLaMA-2-7B-shaped decode stack -- 32 layers of fused QKV (4096x12288), O
+(4096x4096), fused gate+up (4096x22016) and down (11008x4096), group 128,
+random-init int4 weights resident in HBM, one fixed activation row per K --
+streamed back to back. One step = the 128 linear calls of one pass over the
+stack, replayed from a HIP graph; the weight set (3.36 GB) is far larger than
+the 256 MB last-level cache, so every step reads cold weights.
+
+Also reported: the prefill GEMM in TFLOP/s at M=2048 (and 512) on
+LLaMA-2-13B-shaped layers, per-kernel durations from HIP events recorded at the
+kernels' own start and end, a roofline entry for the dominant kernel, and the
+plain fp64 CPU oracle timed on a bounded sample of the same workload.
+
+The decode-generation context for this layer is "TinyChat: Efficient and
+Lightweight Chatbot with AWQ", section "Speed Benchmarks" (per-token latency of
+the generation stage with a W4A16 kernel); the byte accounting follows
+"Applied LLM Quantisation Sagemaker", section "How does it help?".
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
+KERNEL_SOURCES = {
+    "decode": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_decode.hip"),
+    "prefill": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_prefill.hip"),
+}
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def weight_set_bytes(K, N, G):
+    """4-bit codes + fp16 scales + 4-bit zero points (0.5195 B/weight at G=128)."""
+    return K * N // 2 + 2 * N * (K // G) + N * (K // G) // 2
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        import torch  # noqa: F401  (loads the runtime)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            evs.append(e)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+
+class Layer:
+    """One quantised linear layer resident on the GPU, with pre-bound C-ABI
+    arguments (raw pointers) so launch overhead stays out of the way."""
+
+    def __init__(self, awq, torch, K, N, G, gen, x, y, ws, dev, plan=None, scales=(0.001, 0.02)):
+        q = torch.randint(0, 16, (K, N), dtype=torch.uint8, device=dev, generator=gen)
+        self.qw = awq.pack(q)
+        del q
+        z = torch.randint(0, 16, (K // G, N), dtype=torch.uint8, device=dev, generator=gen)
+        self.zw = awq.pack_zeros(z)
+        del z
+        self.s = torch.empty((K // G, N), dtype=torch.float32, device=dev).uniform_(*scales, generator=gen).half()
+        self.K, self.N, self.G = K, N, G
+        self.M = x.shape[0]
+        self.x, self.y = x, y
+        self.plan = awq._plan(plan) if plan is not None else None
+        nbytes = awq.linear_workspace_bytes(self.M, K, N, G, self.plan)
+        buf = ws.get(nbytes) if nbytes else None
+        self.ws_ptr = buf.data_ptr() if buf is not None else None
+        self.ws_len = buf.numel() if buf is not None else 0
+        self.args = (x.data_ptr(), self.qw.data_ptr(), self.s.data_ptr(), self.zw.data_ptr(), self.M, K, N, G,
+                     y.data_ptr(), self.ws_ptr, self.ws_len)
+
+    def launch(self, lib, stream):
+        st = lib.awq_linear_ex(*self.args, ctypes.byref(self.plan) if self.plan else None, stream)
+        if st:
+            raise RuntimeError(f"awq_linear failed: {lib.awq_status_string(st).decode()}")
+
+    def launch_timed(self, lib, stream, e0, e1):
+        st = lib.awq_linear_timed(*self.args, ctypes.byref(self.plan) if self.plan else None, stream, e0, e1)
+        if st:
+            raise RuntimeError(f"awq_linear_timed failed: {lib.awq_status_string(st).decode()}")
+
+
+def build_stack(awq, torch, workload, M, dev, seed, plan=None, layers=None):
+    import synth  # noqa: F401
+    G = workload.G
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    ws = awq.Workspace(dev)
+    xs, ys = {}, {}
+    for sh in workload.shapes:
+        if sh.K not in xs:
+            xs[sh.K] = torch.randn((M, sh.K), dtype=torch.float32, device=dev, generator=gen).half()
+        ys[sh.name] = torch.empty((M, sh.N), dtype=torch.float16, device=dev)
+    # the workspace is sized for the largest need before any pointer is taken
+    need = max(awq.linear_workspace_bytes(M, sh.K, sh.N, G, plan) for sh in workload.shapes)
+    ws.get(need)
+    lay = []
+    for li in range(layers or workload.layers):
+        for sh in workload.shapes:
+            lay.append((sh.name, Layer(awq, torch, sh.K, sh.N, G, gen, xs[sh.K], ys[sh.name], ws, dev, plan,
+                                       (workload.lo, workload.hi))))
+    torch.cuda.synchronize()
+    return lay, ws
+
+
+def per_kernel_times(lib, torch, hip, layers, reps):
+    """Eager pass: every call launched through hipExtLaunchKernelGGL with
+    events at the kernel's own start and end; returns {shape: [ms, ...]}."""
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    n = len(layers) * reps
+    evs = hip.create(2 * n)
+    i = 0
+    for _ in range(reps):
+        for name, L in layers:
+            L.launch_timed(lib, stream, evs[2 * i], evs[2 * i + 1])
+            i += 1
+    torch.cuda.synchronize()
+    out = {}
+    i = 0
+    for _ in range(reps):
+        for name, L in layers:
+            out.setdefault(name, []).append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]))
+            i += 1
+    return out
+
+
+def cpu_baseline(workload, seconds):
+    """The fp64 oracle on host cores, on one layer of the stack (M=1),
+    repeated until about `seconds` of CPU work; weight GB/s."""
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    data = []
+    for si, sh in enumerate(workload.shapes):
+        q, z, s = synth.layer(sh.K, sh.N, workload.G, seed=0, layer_id=si, lo=workload.lo, hi=workload.hi)
+        x = synth.activations(1, sh.K, seed=0, stream=si)
+        data.append((x, q, z, s))
+    total_bytes = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for (x, q, z, s), sh in zip(data, workload.shapes):
+            oracle.linear64(x, q, z, s, workload.G)
+            total_bytes += weight_set_bytes(sh.K, sh.N, workload.G)
+        passes += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(total_bytes / dt / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{passes} pass(es) over one layer of the stack ({len(workload.shapes)} linears, M=1, "
+                   f"{sum(weight_set_bytes(s.K, s.N, workload.G) for s in workload.shapes) / 1e6:.1f} MB of "
+                   f"weights), numpy fp64 dequantise + BLAS matmul, {dt:.1f} s; BLAS threads={threads}, "
+                   f"elementwise steps single-threaded"),
+    }
+
+
+def traffic_entry(kernel, bytes_alg):
+    """HBM traffic per launch from committed rocprofv3 counter summaries, if
+    they were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
+    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer's multi-GPU "
+              f"sharding is a design note, not a built path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import weight_only_bit_awq_amd as awq
+
+    lib = awq.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    hip = HipEvents()
+    wl = synth.LLAMA2_7B_DECODE
+    M = 1
+
+    eprint(f"[bench] building {wl.name}: {wl.layers} layers x {len(wl.shapes)} shapes, M={M}")
+    layers, ws = build_stack(awq, torch, wl, M, dev, args.seed)
+    step_bytes = sum(weight_set_bytes(L.K, L.N, L.G) for _, L in layers)
+    eprint(f"[bench] weight set {step_bytes / 1e9:.3f} GB resident")
+
+    # Capture one step (all 128 launches) in a HIP graph.
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        s = ctypes.c_void_p(side.cuda_stream)
+        for _, L in layers:
+            L.launch(lib, s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _, L in layers:
+            L.launch(lib, s)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    event_ms = e0.elapsed_time(e1) / args.steps
+    value = step_bytes / (wall_ms / 1e3) / 1e9
+    eprint(f"[bench] decode stack: {wall_ms:.4f} ms/step wall, {event_ms:.4f} ms/step events, {value:.1f} GB/s")
+
+    # Per-kernel durations (events at the kernels' own start/end).
+    times = per_kernel_times(lib, torch, hip, layers, args.kernel_reps)
+    per_shape = {}
+    for sh in wl.shapes:
+        ts = sorted(times[sh.name])
+        avg = sum(ts) / len(ts)
+        wb = weight_set_bytes(sh.K, sh.N, wl.G)
+        alg = wb + 2 * M * sh.K + 2 * M * sh.N
+        per_shape[sh.name] = {
+            "K": sh.K, "N": sh.N, "launches": len(ts), "avg_us": round(avg * 1e3, 3),
+            "p10_us": round(ts[len(ts) // 10] * 1e3, 3), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
+            "weight_GBps": round(wb / (avg / 1e3) / 1e9, 1), "alg_GBps": round(alg / (avg / 1e3) / 1e9, 1),
+            "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
+        }
+    kern_sum_ms = sum(p["avg_us"] for p in per_shape.values()) * wl.layers / 1e3
+    dom = max(per_shape, key=lambda k: per_shape[k]["avg_us"])
+    d = per_shape[dom]
+    alg_bytes = weight_set_bytes(d["K"], d["N"], wl.G) + 2 * M * d["K"] + 2 * M * d["N"]
+    achieved = alg_bytes / (d["avg_us"] / 1e6) / 1e9
+    roofline = {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry("decode", alg_bytes),
+        "kernel": f"decode_kernel ({dom}: K={d['K']} N={d['N']} M={M})", "alg_bytes_per_launch": alg_bytes,
+        "avg_launch_us": d["avg_us"],
+    }
+    eprint(f"[bench] per-kernel: " + ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s"
+                                               for k, v in per_shape.items()))
+
+    prefill = None
+    if not args.no_prefill:
+        del graph
+        layers = None
+        torch.cuda.empty_cache()
+        pw = synth.LLAMA2_13B_PREFILL
+        prefill = {"metric": "GEMM TFLOP/s at M=2048", "unit": "TFLOP/s", "workload": pw.name, "shapes": {}}
+        for Mp in pw.Ms:
+            play, _ = build_stack(awq, torch, pw, Mp, dev, args.seed + 1, layers=1)
+            # 1% outlier input channels scaled by 20 in each activation matrix
+            for K in {L.K for _, L in play}:
+                gen = torch.Generator(device=dev)
+                gen.manual_seed(K)
+                cols = torch.randperm(K, device=dev, generator=gen)[: round(0.01 * K)]
+                for _, L in play:
+                    if L.K == K:
+                        L.x[:, cols] *= 20
+                        break
+            pt = per_kernel_times(lib, torch, hip, play, args.prefill_reps)
+            tot_flop, tot_ms = 0.0, 0.0
+            for name, L in play:
+                avg = sum(pt[name]) / len(pt[name])
+                fl = 2.0 * Mp * L.K * L.N
+                tot_flop += fl
+                tot_ms += avg
+                prefill["shapes"][f"{name}@M={Mp}"] = {"K": L.K, "N": L.N, "avg_us": round(avg * 1e3, 2),
+                                                        "TFLOPs": round(fl / (avg / 1e3) / 1e12, 1)}
+            prefill[f"M={Mp}"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
+            del play
+            torch.cuda.empty_cache()
+        prefill["value"] = prefill["M=2048"]
+        big = max((k for k in prefill["shapes"] if k.endswith("M=2048")),
+                  key=lambda k: prefill["shapes"][k]["avg_us"])
+        pv = prefill["shapes"][big]["TFLOPs"]
+        prefill["roofline"] = {"bound": "mfma", "achieved": pv, "peak": FP16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                               "frac": round(pv / FP16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                               "kernel": f"prefill_kernel ({big})"}
+        eprint(f"[bench] prefill: M=2048 {prefill['M=2048']} TFLOP/s, M=512 {prefill['M=512']} TFLOP/s")
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        eprint("[bench] copy calibration: 1 GiB device copy done")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    out = {
+        "metric": "W4A16 GEMV weight GB/s (% HBM peak) at M=1; GEMM TFLOP/s at M=2048",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall_ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic (seeded random-init int4 weights, fp16 N(0,1) activations)",
+        "config": {"workload": wl.name, "layers": wl.layers, "M": M, "group": wl.G,
+                   "shapes": {sh.name: [sh.K, sh.N] for sh in wl.shapes},
+                   "weight_bytes_per_step": step_bytes, "graph": True},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "event_ms_per_step": round(event_ms, 5),
+        "kernel_sum_ms_per_step": round(kern_sum_ms, 5),
+        "per_kernel": per_shape,
+        "roofline": roofline,
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,164 @@
+/*
+ * awq.h -- C ABI of the MI355X (gfx950) W4A16 group-quantised linear layer.
+ *
+ * The operation: y[M,N] = x[M,K] . W[K,N] with
+ *     W[k,n] = (q[k,n] - z[k/G, n]) * s[k/G, n],
+ * q and z unsigned 4-bit codes, s fp16 scales, x and y fp16, fp32 accumulation.
+ * "TinyChat: Efficient and Lightweight Chatbot with AWQ", section "Usage",
+ * steps 3-4: weights quantised to 4 bits in groups of 128 input channels
+ * (64 for Falcon-7B) and run as W4A16 (4-bit weights, 16-bit activations);
+ * section "Speed Benchmarks": the W4A16 GPU kernel serves the generation
+ * stage. The pages print neither the dequantisation rule nor a packing
+ * order; the asymmetric affine rule above and the layouts below are the
+ * readings this library adopts.
+ *
+ * Conventions for every entry point
+ *   - All array pointers are DEVICE pointers (hipMalloc / torch CUDA tensors),
+ *     row-major and contiguous, 16-byte aligned. The caller owns every buffer;
+ *     the library allocates no device memory and keeps no per-call state.
+ *   - fp16 values are passed as their uint16_t bit patterns.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on `stream` and returns without synchronising; inputs
+ *     must stay unchanged until the stream has reached the call.
+ *   - Return value: AWQ_OK (0) or a negative AWQ_ERR_* code. Arguments are
+ *     validated before anything is enqueued; on error nothing is launched.
+ *     M, K or N equal to 0 is a valid empty call that launches nothing.
+ *   - Shapes: K % group == 0; group is 32, 64 or a multiple of 128; N % 8 == 0.
+ *
+ * Layouts
+ *   q (unpacked codes)   uint8 [K, N]; only the low 4 bits of each byte are used.
+ *   scales               fp16  [K/G, N].
+ *   zeros (packed)       uint32 [K/G, N/8]; bits 4i..4i+3 of word (g, c) hold
+ *                        z[g, 8c+i] (least-significant nibble first).
+ *   qweight (device)     awq_qweight_words(K, N) uint32 words in tiles of
+ *                        16 columns x 128 rows: KT = ceil(K/128), NT = ceil(N/16),
+ *                        tile (t, kt) starts at word (t*KT + kt)*256. Word w of
+ *                        a tile, lane l = w/4, slot j = w%4, holds column
+ *                        n = 16t + l%16 and rows k0..k0+7, k0 = 128kt + 32j + 8(l/16);
+ *                        row k0+e sits in nibble position 4(e%2) + e/2.
+ *                        Padding rows (k >= K) and columns (n >= N) hold 0.
+ *                        One 64-lane 16-byte load reads one whole tile, and each
+ *                        word unpacks into two-row fp16 pairs (k0, k0+1), ...
+ *                        with a mask-and-or per pair. The choice follows the
+ *                        idea of interleaved weight repacking for wide loads
+ *                        ("PowerInfer_SmallThinker-4BA0.6B-Instruct-GGUF" page,
+ *                        section "ARM/AVX information").
+ */
+#ifndef AWQ_MI355X_AWQ_H
+#define AWQ_MI355X_AWQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum awq_status {
+  AWQ_OK = 0,
+  AWQ_ERR_NULL = -1,      /* a required pointer is NULL                        */
+  AWQ_ERR_SHAPE = -2,     /* negative size, N % 8 != 0, K % group != 0, ...   */
+  AWQ_ERR_GROUP = -3,     /* group not 32, 64 or a positive multiple of 128   */
+  AWQ_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                 */
+  AWQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required          */
+  AWQ_ERR_HIP = -6,       /* the HIP runtime reported an error (see below)    */
+  AWQ_ERR_PLAN = -7       /* an explicit plan field is out of range           */
+};
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* awq_status_string(int status);
+
+/* hipError_t of the most recent AWQ_ERR_HIP on the calling thread (0 if none). */
+int awq_last_hip_error(void);
+
+/* ABI version: bumped when a signature or a layout changes. */
+int awq_abi_version(void);
+
+/* Number of uint32 words of the device qweight layout for a [K, N] matrix. */
+size_t awq_qweight_words(int64_t K, int64_t N);
+
+/*
+ * awq_pack: codes q uint8 [K, N] -> device-layout qweight (awq_qweight_words
+ * words, written entirely, padding included). K % 8 == 0, N % 8 == 0.
+ * The "real" INT4 weights of TinyChat README "Usage" step 3 (--q_backend real),
+ * arranged for 16-byte gfx950 vector loads.
+ */
+int awq_pack(const uint8_t* q, int64_t K, int64_t N, uint32_t* qweight, void* stream);
+
+/* awq_unpack: inverse of awq_pack; writes q uint8 [K, N] with values 0..15. */
+int awq_unpack(const uint32_t* qweight, int64_t K, int64_t N, uint8_t* q, void* stream);
+
+/* awq_pack_zeros: zero points z uint8 [groups, N] -> packed uint32 [groups, N/8]. */
+int awq_pack_zeros(const uint8_t* z, int64_t groups, int64_t N, uint32_t* zeros, void* stream);
+
+/*
+ * awq_dequant: device qweight + scales + packed zeros -> W fp16 [K, N], with
+ * W[k,n] = round_to_nearest_even_fp16((q[k,n] - z[k/G,n]) * s[k/G,n])
+ * (the exact product rounded once; IEEE special values, subnormals kept).
+ */
+int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                int64_t K, int64_t N, int group, uint16_t* w, void* stream);
+
+/*
+ * Execution plan of awq_linear. Zero fields mean "choose automatically".
+ *   path:    1 = decode path (dequantise in registers, MFMA 16x16x32, M <= 64),
+ *            2 = prefill path (LDS-tiled dequant-then-MFMA GEMM, any M).
+ *   split_k: 0 or 1 (reserved for a cross-workgroup K split; not used).
+ *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
+ *            the K range of the workgroup's 16 columns and their partial sums
+ *            are added through LDS in a fixed order.
+ */
+typedef struct awq_plan {
+  int32_t path;
+  int32_t split_k;
+  int32_t waves;
+  int32_t reserved[5];
+} awq_plan;
+
+/* Resolves the automatic fields of *plan for this shape (plan may be all-zero). */
+int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
+
+/*
+ * Workspace bytes awq_linear needs for this shape and plan (0 if none;
+ * every current plan needs none). A workspace, when one is needed, must be
+ * zero-filled once after allocation, and calls that overlap in time must not
+ * share it.
+ */
+int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes);
+int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group,
+                                  const awq_plan* plan, size_t* bytes);
+
+/*
+ * awq_linear: y[M,N] (fp16) = x[M,K] (fp16) . W[K,N], W dequantised from
+ * qweight/scales/zeros as in awq_dequant, accumulated in fp32, rounded once
+ * to fp16 (round to nearest even). Result within 2e-3 of the exact value
+ * relative to sum_k |x[m,k] * W[k,n]|; the summation order is not specified.
+ */
+int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+               const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+               uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* awq_linear with an explicit plan (for tuning and for testing both paths). */
+int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                  const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                  uint16_t* y, void* workspace, size_t workspace_bytes,
+                  const awq_plan* plan, void* stream);
+
+/*
+ * awq_linear_timed: awq_linear_ex that also records two hipEvent_t handles
+ * (passed as void*, either may be NULL) at the start and at the end of the
+ * layer's kernel itself (hipExtLaunchKernelGGL), so that hipEventElapsedTime
+ * gives the kernel's own duration. Every awq_linear call is one kernel launch
+ * (split-K partials are reduced inside that kernel). For measurement only:
+ * not for use under stream capture.
+ */
+int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                     const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                     uint16_t* y, void* workspace, size_t workspace_bytes,
+                     const awq_plan* plan, void* stream, void* start_event, void* stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AWQ_MI355X_AWQ_H */

@@ -1,0 +1,118 @@
+"""The C ABI library loads, exports every symbol include/awq.h declares, and
+its host-side logic (validation, planning, sizes) behaves as documented.
+No kernel is launched here: every call below fails validation or only plans."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "awq.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import weight_only_bit_awq_amd as awq
+    if not os.path.exists(awq.LIB_PATH):
+        from weight_only_bit_awq_amd import build
+        build.build()
+    return awq.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("awq_pack", "awq_dequant", "awq_linear", "awq_unpack", "awq_pack_zeros",
+                     "awq_linear_workspace_bytes", "awq_qweight_words", "awq_status_string"):
+        assert required in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_binding_covers_header(lib):
+    import weight_only_bit_awq_amd as awq
+    assert set(declared_functions()) <= set(awq._SIGS)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.awq_status_string(0) == b"AWQ_OK"
+    for code in range(-7, 0):
+        assert lib.awq_status_string(code).startswith(b"AWQ_ERR")
+    assert lib.awq_abi_version() == 1
+
+
+def test_qweight_words(lib):
+    import oracle
+    for K, N in [(128, 16), (4096, 4096), (96, 24), (11008, 4096), (32, 8)]:
+        assert lib.awq_qweight_words(K, N) == oracle.device_words(K, N)
+    assert lib.awq_qweight_words(0, 16) == 0
+
+
+def test_validation_errors_before_launch(lib):
+    import weight_only_bit_awq_amd as awq
+    sz = ctypes.c_size_t(0)
+    # group must be 32, 64 or a multiple of 128
+    assert lib.awq_linear_workspace_bytes(1, 480, 16, 96, ctypes.byref(sz)) == -3
+    assert lib.awq_linear_workspace_bytes(1, 4096, 16, 0, ctypes.byref(sz)) == -3
+    # K % group, N % 8, negative sizes
+    assert lib.awq_linear_workspace_bytes(1, 4000, 16, 128, ctypes.byref(sz)) == -2
+    assert lib.awq_linear_workspace_bytes(1, 4096, 12, 128, ctypes.byref(sz)) == -2
+    assert lib.awq_linear_workspace_bytes(-1, 4096, 16, 128, ctypes.byref(sz)) == -2
+    # null pointers
+    assert lib.awq_pack(None, 128, 16, None, None) == -1
+    assert lib.awq_unpack(None, 128, 16, None, None) == -1
+    assert lib.awq_pack_zeros(None, 1, 16, None, None) == -1
+    assert lib.awq_dequant(None, None, None, 128, 16, 128, None, None) == -1
+    assert lib.awq_linear(None, None, None, None, 1, 128, 16, 128, None, None, 0, None) == -1
+    # misaligned pointers are rejected before any launch
+    fake = ctypes.c_void_p(0x1000)
+    odd = ctypes.c_void_p(0x1001)
+    assert lib.awq_linear(odd, fake, fake, fake, 1, 128, 16, 128, fake, None, 0, None) == -4
+    # empty calls succeed without touching pointers
+    assert lib.awq_linear(None, None, None, None, 0, 128, 16, 128, None, None, 0, None) == 0
+    assert lib.awq_pack(None, 0, 16, None, None) == 0
+    # bad plans
+    p = awq.Plan()
+    p.path = 1
+    assert lib.awq_linear_plan(65, 4096, 4096, 128, ctypes.byref(p)) == -7
+    p = awq.Plan()
+    p.path = 1
+    p.waves = 3
+    assert lib.awq_linear_plan(1, 4096, 4096, 128, ctypes.byref(p)) == -7
+    # no cross-workgroup split-K on either path
+    p = awq.Plan()
+    p.path, p.split_k = 1, 4
+    need = ctypes.c_size_t(0)
+    assert lib.awq_linear_workspace_bytes_ex(1, 4096, 4096, 128, ctypes.byref(p), ctypes.byref(need)) == -7
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 1, 4096, 4096, 128, fake, None, 0, ctypes.byref(p), None) == -7
+
+
+def test_plans(lib):
+    import weight_only_bit_awq_amd as awq
+    plan = awq.linear_plan(1, 4096, 4096, 128)
+    assert plan["path"] == 1 and plan["split_k"] == 1 and plan["waves"] in (1, 2, 4, 8, 16)
+    assert awq.linear_plan(64, 4096, 4096, 128)["path"] == 1
+    assert awq.linear_plan(65, 4096, 4096, 128)["path"] == 2
+    assert awq.linear_plan(2048, 5120, 15360, 128)["path"] == 2
+    # no plan needs a workspace
+    assert awq.linear_workspace_bytes(1, 4096, 12288, 128, {"path": 1, "split_k": 1}) == 0
+    assert awq.linear_workspace_bytes(2048, 5120, 15360, 128) == 0
+
+
+def test_missing_library_raises(tmp_path, monkeypatch):
+    import weight_only_bit_awq_amd as awq
+    monkeypatch.setattr(awq, "_lib", None)
+    monkeypatch.setattr(awq, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(awq.AWQLibraryMissing):
+        awq.library()

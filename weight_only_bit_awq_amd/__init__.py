@@ -1,0 +1,258 @@
+"""MI355X (gfx950) W4A16 group-quantised linear layer.
+
+A thin Python binding over the C ABI of ``libawq_mi355x.so`` (declared in
+``include/awq.h``): it checks tensor dtypes, devices and shapes, passes raw
+device pointers and the current HIP stream, and turns status codes into
+exceptions. Every step of the computation runs in the library's HIP kernels;
+PyTorch only provides device memory and streams. If the library has not been
+built, every call raises ``AWQLibraryMissing``.
+
+Functions keep the C names without the ``awq_`` prefix: ``pack``, ``unpack``,
+``pack_zeros``, ``dequant``, ``linear`` (and ``linear_plan``,
+``linear_workspace_bytes``, ``qweight_words``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_NAME = "libawq_mi355x.so"
+LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+
+AWQ_OK = 0
+
+
+class AWQLibraryMissing(RuntimeError):
+    pass
+
+
+class AWQError(RuntimeError):
+    def __init__(self, status: int, message: str, hip_error: int = 0):
+        super().__init__(f"{message} (status {status}, hip error {hip_error})")
+        self.status = status
+        self.hip_error = hip_error
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int32), ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+_SIGS = {
+    "awq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "awq_last_hip_error": (ctypes.c_int, []),
+    "awq_abi_version": (ctypes.c_int, []),
+    "awq_qweight_words": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64]),
+    "awq_pack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_unpack": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_pack_zeros": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                      ctypes.c_void_p]),
+    "awq_dequant": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64,
+                                   ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_linear_plan": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                       ctypes.POINTER(Plan)]),
+    "awq_linear_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                  ctypes.POINTER(ctypes.c_size_t)]),
+    "awq_linear_workspace_bytes_ex": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                     ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_size_t)]),
+    "awq_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                  ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "awq_linear_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                     ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                     ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan), ctypes.c_void_p]),
+    "awq_linear_timed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                        ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+}
+
+
+def library():
+    """Load ``libawq_mi355x.so`` (once). Raises AWQLibraryMissing if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise AWQLibraryMissing(
+                    f"{LIB_PATH} is not built; run `python -m weight_only_bit_awq_amd.build`")
+            # Load PyTorch first so that the library binds to the HIP runtime
+            # PyTorch uses (same soname): one runtime per process, so device
+            # pointers and streams from torch are valid in the library.
+            import torch  # noqa: F401
+            lib = ctypes.CDLL(LIB_PATH)
+            for name, (res, args) in _SIGS.items():
+                fn = getattr(lib, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = lib
+    return _lib
+
+
+def _check(status: int):
+    if status != AWQ_OK:
+        lib = library()
+        raise AWQError(status, lib.awq_status_string(status).decode(), lib.awq_last_hip_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, dtype, name, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims")
+
+
+def _plan(plan):
+    if plan is None:
+        return None
+    if isinstance(plan, Plan):
+        return plan
+    p = Plan()
+    p.path = int(plan.get("path", 0))
+    p.split_k = int(plan.get("split_k", 0))
+    p.waves = int(plan.get("waves", 0))
+    return p
+
+
+def abi_version() -> int:
+    return library().awq_abi_version()
+
+
+def qweight_words(K: int, N: int) -> int:
+    return int(library().awq_qweight_words(K, N))
+
+
+def pack(q):
+    """q uint8 [K, N] (GPU) -> device-layout qweight (int32 tensor of bit patterns)."""
+    torch = _torch()
+    _need(q, torch.uint8, "q", 2)
+    K, N = q.shape
+    out = torch.empty(max(qweight_words(K, N), 1), dtype=torch.int32, device=q.device)
+    _check(library().awq_pack(q.data_ptr(), K, N, out.data_ptr(), _stream(q.device)))
+    return out
+
+
+def unpack(qweight, K: int, N: int):
+    torch = _torch()
+    _need(qweight, torch.int32, "qweight")
+    out = torch.empty((K, N), dtype=torch.uint8, device=qweight.device)
+    _check(library().awq_unpack(qweight.data_ptr(), K, N, out.data_ptr(), _stream(qweight.device)))
+    return out
+
+
+def pack_zeros(z):
+    """z uint8 [K/G, N] -> packed zero points int32 [K/G, N/8]."""
+    torch = _torch()
+    _need(z, torch.uint8, "z", 2)
+    groups, N = z.shape
+    out = torch.empty((groups, N // 8), dtype=torch.int32, device=z.device)
+    _check(library().awq_pack_zeros(z.data_ptr(), groups, N, out.data_ptr(), _stream(z.device)))
+    return out
+
+
+def dequant(qweight, scales, zeros, K: int, N: int, group: int = 128):
+    """Device qweight + fp16 scales [K/G, N] + packed zeros -> fp16 W [K, N]."""
+    torch = _torch()
+    _need(qweight, torch.int32, "qweight")
+    _need(scales, torch.float16, "scales", 2)
+    _need(zeros, torch.int32, "zeros", 2)
+    out = torch.empty((K, N), dtype=torch.float16, device=qweight.device)
+    _check(library().awq_dequant(qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), K, N, group,
+                                 out.data_ptr(), _stream(qweight.device)))
+    return out
+
+
+def linear_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
+    p = _plan(plan) or Plan()
+    _check(library().awq_linear_plan(M, K, N, group, ctypes.byref(p)))
+    return {"path": p.path, "split_k": p.split_k, "waves": p.waves}
+
+
+def linear_workspace_bytes(M: int, K: int, N: int, group: int = 128, plan=None) -> int:
+    out = ctypes.c_size_t(0)
+    p = _plan(plan)
+    _check(library().awq_linear_workspace_bytes_ex(M, K, N, group, ctypes.byref(p) if p else None,
+                                                   ctypes.byref(out)))
+    return int(out.value)
+
+
+class Workspace:
+    """A zero-filled device buffer reused across calls on one stream (the
+    library leaves its counters at zero after every call)."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if nbytes == 0:
+            return None
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def linear(x, qweight, scales, zeros, N: int, group: int = 128, out=None, workspace=None, plan=None):
+    """y[M, N] fp16 = x[M, K] fp16 . W, W from (qweight, scales, zeros)."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(qweight, torch.int32, "qweight")
+    _need(scales, torch.float16, "scales", 2)
+    _need(zeros, torch.int32, "zeros", 2)
+    M, K = x.shape
+    if scales.shape != (K // group, N) or zeros.shape != (K // group, N // 8):
+        raise ValueError("scales must be [K/G, N] and zeros [K/G, N/8]")
+    if qweight.numel() < qweight_words(K, N):
+        raise ValueError("qweight is smaller than the device layout needs")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out", 2)
+    p = _plan(plan)
+    nbytes = linear_workspace_bytes(M, K, N, group, p)
+    ws_ptr, ws_len = None, 0
+    if nbytes:
+        if workspace is None:
+            workspace = Workspace(x.device)
+        buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        ws_ptr, ws_len = buf.data_ptr(), buf.numel() * buf.element_size()
+    lib = library()
+    st = _stream(x.device)
+    if p is None:
+        status = lib.awq_linear(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), M, K, N,
+                                group, out.data_ptr(), ws_ptr, ws_len, st)
+    else:
+        status = lib.awq_linear_ex(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), M, K, N,
+                                   group, out.data_ptr(), ws_ptr, ws_len, ctypes.byref(p), st)
+    _check(status)
+    return out
+
+
+__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "linear", "linear_plan",
+           "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",
+           "abi_version"]

@@ -1,0 +1,224 @@
+// C ABI of the W4A16 group-quantised linear layer: argument validation,
+// execution planning and dispatch to the gfx950 kernels. Declared in
+// include/awq.h; every entry point validates before it enqueues anything and
+// reports failures as negative status codes, never by throwing or aborting.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+
+#include "../../include/awq.h"
+#include "awq_launch.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return AWQ_OK;
+  g_last_hip_error = (int)e;
+  return AWQ_ERR_HIP;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool group_ok(int G) { return G == 32 || G == 64 || (G > 0 && G % 128 == 0); }
+
+int check_dims(int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K < 0 || N < 0) return AWQ_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return AWQ_ERR_SHAPE;
+  if (K * N > ((int64_t)1 << 40)) return AWQ_ERR_SHAPE;
+  return AWQ_OK;
+}
+
+int check_layer(int64_t K, int64_t N, int G) {
+  if (!group_ok(G)) return AWQ_ERR_GROUP;
+  if (K % G != 0 || N % 8 != 0) return AWQ_ERR_SHAPE;
+  return AWQ_OK;
+}
+
+struct Resolved {
+  int path, split, waves;
+  size_t ws_bytes;
+  size_t counter_bytes;
+};
+
+constexpr int kDecodeMaxM = 64;
+
+int resolve_plan(int64_t M, int64_t K, int64_t N, const awq_plan* in, Resolved* out) {
+  awq_plan p = {};
+  if (in) p = *in;
+  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0) return AWQ_ERR_PLAN;
+  if (p.path == 0) p.path = (M <= kDecodeMaxM) ? 1 : 2;
+  if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
+  const int64_t KT = (K + 127) / 128;
+  const int64_t NT = (N + 15) / 16;
+  out->path = p.path;
+  out->split = 1;
+  out->waves = 0;
+  out->ws_bytes = 0;
+  out->counter_bytes = 0;
+  if (p.path == 1) {
+    // The K range of a column tile is split over the waves of its workgroup
+    // and summed through LDS in a fixed order; there is no cross-workgroup
+    // split on this path.
+    if (p.split_k > 1) return AWQ_ERR_PLAN;
+    int waves = p.waves;
+    if (waves) {
+      if (waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16) return AWQ_ERR_PLAN;
+    } else {
+      // About 2048 waves in flight over the 256 CUs, at least 4 and at most
+      // 16 per workgroup, and at least two 128-row tiles per wave.
+      waves = 4;
+      while (waves < 16 && NT * waves < 2048 && KT >= 4 * waves) waves *= 2;
+    }
+    out->waves = waves;
+  } else {
+    if (p.split_k > 1 || p.waves) return AWQ_ERR_PLAN;
+  }
+  return AWQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* awq_status_string(int status) {
+  switch (status) {
+    case AWQ_OK: return "AWQ_OK";
+    case AWQ_ERR_NULL: return "AWQ_ERR_NULL: a required pointer is NULL";
+    case AWQ_ERR_SHAPE: return "AWQ_ERR_SHAPE: invalid sizes (negative, N % 8, K % group, ...)";
+    case AWQ_ERR_GROUP: return "AWQ_ERR_GROUP: group must be 32, 64 or a positive multiple of 128";
+    case AWQ_ERR_ALIGN: return "AWQ_ERR_ALIGN: a pointer is not suitably aligned";
+    case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE: workspace missing or too small";
+    case AWQ_ERR_HIP: return "AWQ_ERR_HIP: the HIP runtime reported an error";
+    case AWQ_ERR_PLAN: return "AWQ_ERR_PLAN: an explicit plan field is out of range";
+  }
+  return "AWQ: unknown status";
+}
+
+int awq_last_hip_error(void) { return g_last_hip_error; }
+
+int awq_abi_version(void) { return 1; }
+
+size_t awq_qweight_words(int64_t K, int64_t N) {
+  if (K <= 0 || N <= 0) return 0;
+  return (size_t)((K + 127) / 128) * (size_t)((N + 15) / 16) * 256;
+}
+
+int awq_pack(const uint8_t* q, int64_t K, int64_t N, uint32_t* qweight, void* stream) {
+  int st = check_dims(0, K, N);
+  if (st) return st;
+  if (K % 8 || N % 8) return AWQ_ERR_SHAPE;
+  if (K == 0 || N == 0) return AWQ_OK;
+  if (!q || !qweight) return AWQ_ERR_NULL;
+  if (!aligned(qweight, 16)) return AWQ_ERR_ALIGN;
+  return hip_status(awq::launch_pack(q, (int)K, (int)N, qweight, (hipStream_t)stream));
+}
+
+int awq_unpack(const uint32_t* qweight, int64_t K, int64_t N, uint8_t* q, void* stream) {
+  int st = check_dims(0, K, N);
+  if (st) return st;
+  if (K % 8 || N % 8) return AWQ_ERR_SHAPE;
+  if (K == 0 || N == 0) return AWQ_OK;
+  if (!q || !qweight) return AWQ_ERR_NULL;
+  if (!aligned(qweight, 16)) return AWQ_ERR_ALIGN;
+  return hip_status(awq::launch_unpack(qweight, (int)K, (int)N, q, (hipStream_t)stream));
+}
+
+int awq_pack_zeros(const uint8_t* z, int64_t groups, int64_t N, uint32_t* zeros, void* stream) {
+  int st = check_dims(0, groups, N);
+  if (st) return st;
+  if (N % 8) return AWQ_ERR_SHAPE;
+  if (groups == 0 || N == 0) return AWQ_OK;
+  if (!z || !zeros) return AWQ_ERR_NULL;
+  if (!aligned(zeros, 4)) return AWQ_ERR_ALIGN;
+  return hip_status(awq::launch_pack_zeros(z, (int)groups, (int)N, zeros, (hipStream_t)stream));
+}
+
+int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t K, int64_t N,
+                int group, uint16_t* w, void* stream) {
+  int st = check_dims(0, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (K == 0 || N == 0) return AWQ_OK;
+  if (!qweight || !scales || !zeros || !w) return AWQ_ERR_NULL;
+  if (!aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) || !aligned(w, 2)) return AWQ_ERR_ALIGN;
+  return hip_status(awq::launch_dequant(qweight, scales, zeros, (int)K, (int)N, group, w, (hipStream_t)stream));
+}
+
+int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (!plan) return AWQ_ERR_NULL;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  plan->path = r.path;
+  plan->split_k = r.split;
+  plan->waves = r.path == 1 ? r.waves : 0;
+  return AWQ_OK;
+}
+
+int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
+                                  size_t* bytes) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (!bytes) return AWQ_ERR_NULL;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  *bytes = (M == 0 || K == 0 || N == 0) ? 0 : r.ws_bytes;
+  return AWQ_OK;
+}
+
+int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes) {
+  return awq_linear_workspace_bytes_ex(M, K, N, group, nullptr, bytes);
+}
+
+int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                     int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                     const awq_plan* plan, void* stream, void* start_event, void* stop_event) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  if (M == 0 || N == 0) return AWQ_OK;
+  if (!y) return AWQ_ERR_NULL;
+  if (K == 0) {
+    // Empty contraction: y = 0.
+    if (!aligned(y, 2)) return AWQ_ERR_ALIGN;
+    return hip_status(awq::launch_fill_zero(y, M * N, (hipStream_t)stream));
+  }
+  if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) || !aligned(y, 2))
+    return AWQ_ERR_ALIGN;
+  if (r.ws_bytes) {
+    if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return AWQ_ERR_ALIGN;
+  }
+  if (r.path == 1 && (M * K * 2 >= ((int64_t)1 << 31) || (K / group) * N * 2 >= ((int64_t)1 << 31)))
+    return AWQ_ERR_SHAPE;  // the decode path addresses x and scales with 32-bit buffer offsets
+  awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
+  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  if (r.path == 1) {
+    return hip_status(awq::launch_decode(a, r.waves, L));
+  }
+  return hip_status(awq::launch_prefill(a, L));
+}
+
+int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                  int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+                  const awq_plan* plan, void* stream) {
+  return awq_linear_timed(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, plan, stream,
+                          nullptr, nullptr);
+}
+
+int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
+               int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+  return awq_linear_ex(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace awq {
+
+hipError_t launch_pack(const uint8_t* q, int K, int N, uint32_t* out, hipStream_t st);
+hipError_t launch_unpack(const uint32_t* in, int K, int N, uint8_t* q, hipStream_t st);
+hipError_t launch_pack_zeros(const uint8_t* z, int groups, int N, uint32_t* out, hipStream_t st);
+hipError_t launch_dequant(const uint32_t* qw, const uint16_t* scales, const uint32_t* zeros, int K, int N,
+                          int G, uint16_t* w, hipStream_t st);
+
+hipError_t launch_fill_zero(uint16_t* y, int64_t n, hipStream_t st);
+
+struct LinearArgs {
+  const uint16_t* x;
+  const uint32_t* qw;
+  const uint16_t* scales;
+  const uint32_t* zeros;
+  uint16_t* y;
+  int M, K, N, G;
+};
+
+// Where and how a kernel is launched. With timing events set, the kernel is
+// launched through hipExtLaunchKernelGGL, which records `start` and `stop` at
+// the kernel's own start and end on `stream`.
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+
+template <typename F, typename... Args>
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, const Launch& L, Args... args) {
+  if (L.start || L.stop)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.stream, L.start, L.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, L.stream, args...);
+  return hipGetLastError();
+}
+
+// Decode path: one 16-column tile per workgroup, `waves` waves splitting its
+// K range and summing through LDS.
+hipError_t launch_decode(const LinearArgs& a, int waves, const Launch& L);
+
+// Prefill path: LDS-tiled dequantise-then-MFMA GEMM.
+hipError_t launch_prefill(const LinearArgs& a, const Launch& L);
+
+}  // namespace awq
