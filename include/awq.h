@@ -32,7 +32,8 @@
  *                        z[g, 8c+i] (least-significant nibble first).
  *   qweight (device)     awq_qweight_words(K, N) uint32 words in tiles of
  *                        16 columns x 128 rows: KT = ceil(K/128), NT = ceil(N/16),
- *                        tile (t, kt) starts at word (t*KT + kt)*256. Word w of
+ *                        tile (t, kt) starts at word (kt*NT + t)*256 (the tiles
+ *                        of one 128-row band are adjacent). Word w of
  *                        a tile, lane l = w/4, slot j = w%4, holds column
  *                        n = 16t + l%16 and rows k0..k0+7, k0 = 128kt + 32j + 8(l/16);
  *                        row k0+e sits in nibble position 4(e%2) + e/2.
@@ -107,12 +108,20 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
  *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
  *            the K range of the workgroup's 16 columns and their partial sums
  *            are added through LDS in a fixed order.
+ *   tpw:     decode path, staged activations: 16-column tiles per workgroup
+ *            (1 or 2).
+ *   x_stage: decode path: 1 = activations and the (scale, zero point) words
+ *            of the workgroup's columns staged in LDS once per workgroup
+ *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,
+ *            scales and zero points read per tile.
  */
 typedef struct awq_plan {
   int32_t path;
   int32_t split_k;
   int32_t waves;
-  int32_t reserved[5];
+  int32_t tpw;
+  int32_t x_stage;
+  int32_t reserved[3];
 } awq_plan;
 
 /* Resolves the automatic fields of *plan for this shape (plan may be all-zero). */

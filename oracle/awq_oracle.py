@@ -104,7 +104,8 @@ def unpack_zeros(words: np.ndarray) -> np.ndarray:
 device_layout_doc = """
 Tiles of 16 output columns x 128 input channels, 256 uint32 words each.
 KT = ceil(K/128) tiles along K, NT = ceil(N/16) tiles along N; tile (t, kt)
-begins at word (t*KT + kt)*256. Word w of a tile: lane l = w // 4, slot
+begins at word (kt*NT + t)*256 (tiles of one 128-row band are adjacent).
+Word w of a tile: lane l = w // 4, slot
 j = w % 4; it holds column n = 16t + (l mod 16) and rows k0 .. k0+7 with
 k0 = 128kt + 32j + 8(l // 16). Row k0+e sits in nibble position
 p(e) = 4(e mod 2) + (e // 2) (bits 4p .. 4p+3). Rows k >= K and columns
@@ -125,8 +126,8 @@ def _device_coords(K: int, N: int):
     NT = -(-N // 16)
     w = np.arange(NT * KT * 256, dtype=np.int64)
     tile = w // 256
-    t = tile // KT
-    kt = tile % KT
+    kt = tile // NT
+    t = tile % NT
     within = w % 256
     lane = within // 4
     slot = within % 4

@@ -90,6 +90,12 @@ def test_validation_errors_before_launch(lib):
     p.path = 1
     p.waves = 3
     assert lib.awq_linear_plan(1, 4096, 4096, 128, ctypes.byref(p)) == -7
+    p = awq.Plan()
+    p.path, p.tpw = 1, 3
+    assert lib.awq_linear_plan(1, 4096, 4096, 128, ctypes.byref(p)) == -7
+    p = awq.Plan()
+    p.path, p.x_stage = 1, 1  # staged activations need M <= 16
+    assert lib.awq_linear_plan(32, 4096, 4096, 128, ctypes.byref(p)) == -7
     # no cross-workgroup split-K on either path
     p = awq.Plan()
     p.path, p.split_k = 1, 4
@@ -102,6 +108,8 @@ def test_plans(lib):
     import weight_only_bit_awq_amd as awq
     plan = awq.linear_plan(1, 4096, 4096, 128)
     assert plan["path"] == 1 and plan["split_k"] == 1 and plan["waves"] in (1, 2, 4, 8, 16)
+    assert plan["x_stage"] == 1 and plan["tpw"] in (1, 2)
+    assert awq.linear_plan(32, 4096, 4096, 128)["x_stage"] == 2
     assert awq.linear_plan(64, 4096, 4096, 128)["path"] == 1
     assert awq.linear_plan(65, 4096, 4096, 128)["path"] == 2
     assert awq.linear_plan(2048, 5120, 15360, 128)["path"] == 2

@@ -41,10 +41,21 @@ def test_decode_path(awq, M, K, N, G):
     x = synth.activations(M, K, seed=N)
     y64 = oracle.linear64(x, q, z, s, G)
     D = oracle.l1_scale(x, q, z, s, G)
-    for plan in ({"path": 1}, {"path": 1, "waves": 1}, {"path": 1, "waves": 2}, {"path": 1, "waves": 8},
-                 {"path": 1, "waves": 16}):
+    plans = [{"path": 1}]
+    for waves in (1, 2, 4, 8, 16):
+        plans.append({"path": 1, "waves": waves, "x_stage": 2})
+        for tpw in (1, 2):
+            plans.append({"path": 1, "waves": waves, "x_stage": 1, "tpw": tpw})
+    ran = 0
+    for plan in plans:
+        try:
+            awq.linear_plan(M, K, N, G, plan)
+        except awq.AWQError:
+            continue  # e.g. activations too large for the LDS-staged variant
         log(f"  plan {plan}")
         check_close(run(awq, x, q, z, s, G, plan), y64, D, what=f"{plan}")
+        ran += 1
+    assert ran >= 6
 
 
 @pytest.mark.parametrize("M,K,N,G", [(1, 128, 16, 128), (65, 256, 136, 128), (130, 384, 40, 64),
@@ -70,7 +81,10 @@ def _exact_case(M, K, N, G, seed=0):
     return x, q, z, s
 
 
-@pytest.mark.parametrize("plan", [{"path": 1}, {"path": 1, "waves": 16}, {"path": 1, "waves": 1}, {"path": 2}])
+@pytest.mark.parametrize("plan", [{"path": 1}, {"path": 1, "waves": 16, "x_stage": 1, "tpw": 2},
+                                  {"path": 1, "waves": 2, "x_stage": 1, "tpw": 1},
+                                  {"path": 1, "waves": 1, "x_stage": 2}, {"path": 1, "waves": 4, "x_stage": 2},
+                                  {"path": 2}])
 def test_exact_case_bitwise(awq, plan):
     M, K, N, G = 9, 768, 72, 128
     log(f"exact M={M} K={K} N={N} plan={plan}")

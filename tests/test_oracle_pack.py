@@ -73,7 +73,20 @@ def test_device_golden_words():
     words = oracle.pack_device(q)
     assert words.size == 256
     for parts in _golden_lines("device_layout_words.txt"):
+        if parts[0] == "tile":
+            continue
         assert int(words[int(parts[0])]) == int(parts[1], 16), parts
+
+
+def test_device_tile_order_golden():
+    K, N = 256, 32
+    kk, nn = np.meshgrid(np.arange(K), np.arange(N), indexing="ij")
+    q = (2 * (kk // 128) + nn // 16).astype(np.uint8)
+    words = oracle.pack_device(q).reshape(4, 256)
+    for parts in _golden_lines("device_layout_words.txt"):
+        if parts[0] != "tile":
+            continue
+        assert np.all(words[int(parts[1])] == int(parts[2], 16)), parts
 
 
 @pytest.mark.parametrize("K,N", [(128, 16), (256, 48), (96, 24), (384, 8), (32, 40)])

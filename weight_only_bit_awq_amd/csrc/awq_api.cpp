@@ -39,17 +39,18 @@ int check_layer(int64_t K, int64_t N, int G) {
 }
 
 struct Resolved {
-  int path, split, waves;
+  int path, split, waves, tpw, x_stage;
   size_t ws_bytes;
   size_t counter_bytes;
 };
 
 constexpr int kDecodeMaxM = 64;
 
-int resolve_plan(int64_t M, int64_t K, int64_t N, const awq_plan* in, Resolved* out) {
+int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out) {
   awq_plan p = {};
   if (in) p = *in;
-  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0) return AWQ_ERR_PLAN;
+  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2)
+    return AWQ_ERR_PLAN;
   if (p.path == 0) p.path = (M <= kDecodeMaxM) ? 1 : 2;
   if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
   const int64_t KT = (K + 127) / 128;
@@ -57,6 +58,8 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, const awq_plan* in, Resolved* 
   out->path = p.path;
   out->split = 1;
   out->waves = 0;
+  out->tpw = 0;
+  out->x_stage = 0;
   out->ws_bytes = 0;
   out->counter_bytes = 0;
   if (p.path == 1) {
@@ -64,18 +67,28 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, const awq_plan* in, Resolved* 
     // and summed through LDS in a fixed order; there is no cross-workgroup
     // split on this path.
     if (p.split_k > 1) return AWQ_ERR_PLAN;
+    if (p.waves && p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8 && p.waves != 16)
+      return AWQ_ERR_PLAN;
+    if (p.tpw > 2) return AWQ_ERR_PLAN;
+    // Automatic choice (measured on the LLaMA-shaped decode layers): about
+    // 2048 waves over the 256 CUs, four waves per workgroup for wide layers
+    // and eight for narrow ones; two column tiles per workgroup when that
+    // still leaves at least two workgroups per CU.
     int waves = p.waves;
-    if (waves) {
-      if (waves != 1 && waves != 2 && waves != 4 && waves != 8 && waves != 16) return AWQ_ERR_PLAN;
-    } else {
-      // About 2048 waves in flight over the 256 CUs, at least 4 and at most
-      // 16 per workgroup, and at least two 128-row tiles per wave.
-      waves = 4;
-      while (waves < 16 && NT * waves < 2048 && KT >= 4 * waves) waves *= 2;
-    }
+    if (!waves) waves = (NT * 4 >= 2048 || KT < 32) ? 4 : 8;
+    int tpw = p.tpw;
+    if (!tpw) tpw = (NT >= 1024) ? 2 : 1;
+    int x_stage = p.x_stage;
+    const bool fits = M >= 1 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
+    if (x_stage == 0) x_stage = fits ? 1 : 2;
+    if (x_stage == 1 && !fits) return AWQ_ERR_PLAN;
+    if (x_stage == 2) tpw = 1;
+    if (x_stage == 2 && p.tpw > 1) return AWQ_ERR_PLAN;
     out->waves = waves;
+    out->tpw = tpw;
+    out->x_stage = x_stage;
   } else {
-    if (p.split_k > 1 || p.waves) return AWQ_ERR_PLAN;
+    if (p.split_k > 1 || p.waves || p.tpw || p.x_stage) return AWQ_ERR_PLAN;
   }
   return AWQ_OK;
 }
@@ -154,10 +167,12 @@ int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) 
   if ((st = check_layer(K, N, group))) return st;
   if (!plan) return AWQ_ERR_NULL;
   Resolved r;
-  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
   plan->path = r.path;
   plan->split_k = r.split;
-  plan->waves = r.path == 1 ? r.waves : 0;
+  plan->waves = r.waves;
+  plan->tpw = r.tpw;
+  plan->x_stage = r.x_stage;
   return AWQ_OK;
 }
 
@@ -168,7 +183,7 @@ int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group, co
   if ((st = check_layer(K, N, group))) return st;
   if (!bytes) return AWQ_ERR_NULL;
   Resolved r;
-  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
   *bytes = (M == 0 || K == 0 || N == 0) ? 0 : r.ws_bytes;
   return AWQ_OK;
 }
@@ -184,7 +199,7 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
   if (st) return st;
   if ((st = check_layer(K, N, group))) return st;
   Resolved r;
-  if ((st = resolve_plan(M, K, N, plan, &r))) return st;
+  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
   if (M == 0 || N == 0) return AWQ_OK;
   if (!y) return AWQ_ERR_NULL;
   if (K == 0) {
@@ -204,7 +219,8 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
   awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
   const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
   if (r.path == 1) {
-    return hip_status(awq::launch_decode(a, r.waves, L));
+    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1};
+    return hip_status(awq::launch_decode(a, cfg, L));
   }
   return hip_status(awq::launch_prefill(a, L));
 }

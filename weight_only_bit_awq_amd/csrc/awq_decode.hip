@@ -5,66 +5,317 @@
 // This is the generation-stage kernel of "TinyChat: Efficient and Lightweight
 // Chatbot with AWQ" (section "Speed Benchmarks": INT4 weights with a W4A16 GPU
 // kernel; latency reported per generated token). Decode reads every weight
-// once per token, so the kernel is bound by HBM bandwidth: the work per
-// weight must stay far below the vector ALU budget (about 2.5 lane-operations
-// per weight at 8 TB/s on 256 CUs at 2.4 GHz).
+// once per token, so the kernel is bound by HBM bandwidth and by the number
+// of memory requests: each 128-row weight tile must cost one 16-byte load per
+// lane and little vector-ALU work (the budget is about 2.5 lane-operations per
+// weight at 8 TB/s on 256 CUs at 2.4 GHz).
 //
 // Design
-//   * A workgroup owns one 16-column tile of the device layout; its WAVES
-//     waves split the K range, taking the 128-row tiles in turn (wave w reads
-//     tiles w, w + WAVES, ...), so a workgroup streams WAVES consecutive KiB at
-//     a time. One 64-lane 16-byte load brings a whole 1 KiB tile.
+//   * A workgroup owns TPW 16-column tiles of the device layout; its WAVES
+//     waves split the K range, taking the 128-row bands in turn (wave w reads
+//     bands w, w + WAVES, ...). Tiles of one band are adjacent in memory, so
+//     at any moment the workgroups read a contiguous stretch of the matrix.
+//     One 64-lane 16-byte load brings a whole 1 KiB tile.
 //   * Lane l holds column l%16 and rows 8(l/16) + 32j .. +7 (j = 0..3) of a
 //     tile: exactly the B operand of v_mfma_f32_16x16x32_f16 for the four
-//     32-row blocks of the tile. The activation rows form the A operand (rows
-//     beyond M are zero), so one MFMA covers 16 rows of x at no extra cost:
-//     the same kernel serves M = 1..16 per 16-row tile, up to four tiles.
-//   * Per word: 1 shift, 4 mask-and-or, 4 packed fp16 subtractions give the
-//     exact (q - z) as fp16 (0.6 VALU operations per weight). The per-group
-//     scale is applied once per group to the fp32 MFMA result.
-//   * Activations, scales and zero points are read with raw buffer loads:
-//     rows >= M and columns >= N get an out-of-range offset and read as zero,
-//     so the loop has no branches. All loads of a tile are issued together,
-//     DEPTH tiles ahead; the loop body is branch-free, so the in-order
-//     vector-memory counter lets each wave wait only for the tile it consumes.
-//     Past a wave's last tile the prefetch index is clamped (a cache hit) and
-//     the consumed result is scaled by zero.
-//   * A ragged last tile (K not a multiple of 128) is handled after the loop
-//     with explicit row masks.
-//   * The waves' fp32 results are summed through LDS and stored as fp16.
-//   * Workgroup ids are remapped so neighbouring tiles run on the same XCD and
-//     share its L2 for scales, zero points and activations.
+//     32-row blocks of the tile. The activation rows form the A operand, so
+//     one MFMA covers 16 rows of x at no extra cost.
+//   * Per word: 1 shift, 4 mask-and-or (v_and_or_b32), 4 packed fp16
+//     subtractions give the exact (q - z) as fp16. The per-group scale is
+//     applied once per group to the fp32 MFMA result.
+//   * Staged variant (M <= 16 and the data fits in LDS): at the start each
+//     workgroup copies the activation rows and, for its columns, one 32-bit
+//     word per (group, column) holding the scale bits and the zero point
+//     into LDS. The loop then issues exactly one global load per tile, DEPTH
+//     tiles ahead, and reads the A operand and the group word from LDS (LDS
+//     reads have their own counter and never wait on the weight stream).
+//   * Streamed variant (larger M or K): activations, scales and zero points
+//     are read per tile with raw buffer loads.
+//   * Rows >= M and columns >= N read as zero (out-of-range buffer offsets) or
+//     are never stored, so loops have no data-dependent branches; past a
+//     wave's last tile the prefetch index is clamped and the result is scaled
+//     by zero. A ragged last band (K not a multiple of 128) is handled after
+//     the loop with explicit masks.
+//   * The waves' fp32 results are summed through LDS in a fixed order and
+//     stored as fp16. Workgroup ids are remapped so neighbouring tiles run on
+//     the same XCD.
+#include <algorithm>
+
 #include "awq_device.h"
 #include "awq_launch.h"
 
 namespace awq {
 
-// Groups per 128-row tile: GPT = 4 (G = 32), 2 (G = 64), 1 (G = 128) or
-// 0 (G a larger multiple of 128: several tiles per group).
-template <int MT, int GPT>
-struct Bundle {
-  u4 wq;             // one 16-byte slice of the tile: 4 words
-  u4 xa[MT][4];      // A operand: 8 fp16 of x per 32-row block and 16-row tile
-  uint32_t s[GPT > 0 ? GPT : 1];   // scale bits per group in the tile
-  uint32_t zw[GPT > 0 ? GPT : 1];  // packed zero-point word per group
+// Groups per 128-row band: GPT = 4 (G = 32), 2 (G = 64), 1 (G = 128) or 0 (G a
+// larger multiple of 128: several bands per group).
+template <int GPT>
+struct GroupsPerBand {
+  static constexpr int NG = GPT > 0 ? GPT : 1;  // group entries per band
+  static constexpr int JPG = 4 / NG;            // 32-row blocks per group entry
+  __device__ static __forceinline__ uint32_t group(int kt, int gi, int tpg) {
+    return GPT == 0 ? (uint32_t)kt / (uint32_t)tpg : (uint32_t)(kt * GPT + gi);
+  }
 };
 
-struct DecodeCtx {
+// (a & m) | o with m and o held in VGPRs (see decode_consts): the compiler
+// then selects one v_and_or_b32 (gfx9 VOP3 encodes no literal operands; with
+// literal masks it emits a separate AND and OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
+
+struct DecodeConsts {
+  uint32_t m1, m2, o1, o2;  // 0x000F000F, 0x00F000F0, 0x64006400, 0x54005400 in VGPRs
+};
+
+__device__ __forceinline__ DecodeConsts decode_consts() {
+  DecodeConsts k;
+  k.m1 = 0x000F000Fu;
+  k.m2 = 0x00F000F0u;
+  k.o1 = 0x64006400u;
+  k.o2 = 0x54005400u;
+  // opaque to the optimiser: keeps the constants in VGPRs
+  asm volatile("" : "+v"(k.m1), "+v"(k.m2), "+v"(k.o1), "+v"(k.o2));
+  return k;
+}
+
+// Eight rows (q - z) of one device word, exact, as fp16 (see awq_device.h).
+__device__ __forceinline__ h8 decode_diff_vk(uint32_t w, ZeroConst c, const DecodeConsts& k) {
+  const uint32_t w8 = w >> 8;
+  const h2 p0 = as_h2(and_or(w, k.m1, k.o1)) + as_h2(c.c1024);
+  const h2 p1 = as_h2(and_or(w, k.m2, k.o2)) + as_h2(c.c64);
+  const h2 p2 = as_h2(and_or(w8, k.m1, k.o1)) + as_h2(c.c1024);
+  const h2 p3 = as_h2(and_or(w8, k.m2, k.o2)) + as_h2(c.c64);
+  h8 r;
+  r[0] = p0[0]; r[1] = p0[1];
+  r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1];
+  r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Weights are read exactly once per call: non-temporal loads stream them
+// past the caches.
+__device__ __forceinline__ u4 load_weights(const u4* p) { return __builtin_nontemporal_load(p); }
+
+__device__ __forceinline__ float scale_of(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// ---------------------------------------------------------------------------
+// Staged variant
+// ---------------------------------------------------------------------------
+
+struct StagedLayout {
+  uint32_t x_row;        // bytes per staged activation row (K padded to >= 128, + 16)
+  uint32_t x_chunks;     // 16-byte chunks per staged row
+  uint32_t meta_off;     // byte offset of the group words
+  uint32_t scratch_off;  // per-thread 16-byte slots for masked staging stores
+};
+
+template <int TPW, int GPT, int WAVES, int DEPTH, int S>
+__global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_t* __restrict__ x,
+                                                                   const u4* __restrict__ qw,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint32_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ y, int M, int K, int N,
+                                                                   int G, int NT, StagedLayout lay) {
+  using GB = GroupsPerBand<GPT>;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int NTH = 64 * WAVES;
+  const int wg = xcd_remap(blockIdx.x, gridDim.x);
+  const int t0 = wg * TPW;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 4;
+  const int groups = K / G;
+  const int tpg = G / 128;
+  const int KT = (K + 127) / 128;
+  const int KTF = K / 128;
+
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
+  const rsrc_t rz = make_rsrc(zeros, (uint32_t)groups * (uint32_t)(N / 8) * 4u);
+
+  // 1. Staging loads (activations and group words), issued first: they come
+  //    from L2 and are waited for before the weight stream is.
+  const uint32_t x_total = (uint32_t)M * lay.x_chunks;
+  const uint32_t m_total = (uint32_t)(TPW * groups * 16);
+  u4 xv[S];
+  uint32_t sv[S], zv[S];
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const uint32_t e = threadIdx.x + i * NTH;
+    const uint32_t row = e / lay.x_chunks, cc = e - row * lay.x_chunks;
+    const bool ok = e < x_total && cc * 8u < (uint32_t)K;
+    xv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (row * K + cc * 8u) * 2u : kOOB, 0, 0));
+    const uint32_t tt = e / (uint32_t)(groups * 16), rem = e - tt * (uint32_t)(groups * 16);
+    const uint32_t g = rem >> 4, col = 16u * (t0 + tt) + (rem & 15u);
+    // Offsets are below 2^31, so setting bit 31 makes a masked load read
+    // zero (written as arithmetic: a select here becomes a branch).
+    const uint32_t bad = (uint32_t)!(e < m_total && col < (uint32_t)N) << 31;
+    sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, ((g * N + col) * 2u) | bad, 0, 0);
+    zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, ((g * (N / 8) + (col >> 3)) * 4u) | bad, 0, 0);
+    zv[i] = (zv[i] >> (4 * (col & 7))) & 0xFu;
+  }
+
+  // 2. Weight prefetch: one 16-byte load per lane per tile, DEPTH bands ahead.
+  //    The index is clamped to the wave's last band (band 0 when it has none,
+  //    which always exists), so the prefetch is unconditional and the waits
+  //    before the staging stores cover only the staging loads.
+  const int n_my = KTF > w ? (KTF - w + WAVES - 1) / WAVES : 0;
+  const int last = max(w + WAVES * (n_my - 1), 0);
+  const u4* qcol[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
+  const int64_t band = (int64_t)NT * 64;
+  u4 buf[DEPTH][TPW];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) buf[d][tt] = load_weights(qcol[tt] + min(w + WAVES * d, last) * band);
+
+  // 3. Staging stores (masked ones go to this thread's scratch slot) and barrier.
+#pragma unroll
+  for (int i = 0; i < S; ++i) {
+    const uint32_t e = threadIdx.x + i * NTH;
+    const uint32_t row = e / lay.x_chunks, cc = e - row * lay.x_chunks;
+    const uint32_t xa = e < x_total ? row * lay.x_row + cc * 16u : lay.scratch_off + threadIdx.x * 16u;
+    *reinterpret_cast<u4*>(smem + xa) = xv[i];
+    const uint32_t ma = e < m_total ? lay.meta_off + e * 4u : lay.scratch_off + threadIdx.x * 16u;
+    *reinterpret_cast<uint32_t*>(smem + ma) = sv[i] | (zv[i] << 16);
+  }
+  __syncthreads();
+
+  // 4. Main loop over full bands.
+  const DecodeConsts kc = decode_consts();
+  const int rowc = min(lane & 15, M - 1);  // rows >= M read row M-1; never stored
+  const char* xrow = smem + rowc * lay.x_row + 16 * h;
+  const char* meta = smem + lay.meta_off + (lane & 15) * 4;
+  f4 acc[TPW];
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt) acc[tt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  auto consume = [&](const u4 (&wq)[TPW], int kt, float valid) {
+    h8 a[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const h8*>(xrow + 256 * kt + 64 * j);
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) {
+#pragma unroll
+      for (int gi = 0; gi < GB::NG; ++gi) {
+        // clamped: the zero-weighted round of a wave without full bands may
+        // visit a ragged band whose last groups do not exist
+        const uint32_t g = min(GB::group(kt, gi, tpg), (uint32_t)groups - 1u);
+        const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta + ((tt * groups + g) * 16) * 4);
+        const ZeroConst zc = zero_const(mw >> 16);
+        f4 accg;
+#pragma unroll
+        for (int jj = 0; jj < GB::JPG; ++jj) {
+          const int j = gi * GB::JPG + jj;
+          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], decode_diff_vk(wq[tt][j], zc, kc),
+                                                        jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg, 0, 0, 0);
+        }
+        acc[tt] += (valid * scale_of(mw & 0xFFFFu)) * accg;
+      }
+    }
+  };
+
+  // Unconditional loop: a wave without bands runs one round scaled by zero on
+  // band 0 (a branch around the loop would let the compiler sink the weight
+  // prefetch below the barrier).
+  const int rounds = max((n_my + DEPTH - 1) / DEPTH, 1);
+  for (int r = 0; r < rounds - 1; ++r) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i = r * DEPTH + d;
+      consume(buf[d], w + WAVES * i, 1.f);
+      const int nk = min(w + WAVES * (i + DEPTH), last);
+#pragma unroll
+      for (int tt = 0; tt < TPW; ++tt) buf[d][tt] = load_weights(qcol[tt] + nk * band);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int i = (rounds - 1) * DEPTH + d;
+    consume(buf[d], min(w + WAVES * i, last), i < n_my ? 1.f : 0.f);
+  }
+
+  // 5. Ragged last band: blocks past K are skipped; groups past the last one
+  //    hold no data and are skipped as well.
+  if (KTF < KT && w == (KTF % WAVES)) {
+    u4 wq[TPW];
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt) wq[tt] = load_weights(qcol[tt] + KTF * band);
+    const int valid_blocks = (K - 128 * KTF) / 32;
+#pragma unroll
+    for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+      for (int gi = 0; gi < GB::NG; ++gi) {
+        if (gi * GB::JPG >= valid_blocks) continue;
+        const uint32_t g = GB::group(KTF, gi, tpg);
+        const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta + ((tt * groups + g) * 16) * 4);
+        const ZeroConst zc = zero_const(mw >> 16);
+        f4 accg = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < GB::JPG; ++jj) {
+          const int j = gi * GB::JPG + jj;
+          if (j < valid_blocks)
+            accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8*>(xrow + 256 * KTF + 64 * j),
+                                                          decode_diff_vk(wq[tt][j], zc, kc), accg, 0, 0, 0);
+        }
+        acc[tt] += scale_of(mw & 0xFFFFu) * accg;
+      }
+  }
+
+  // 6. Sum the waves' results through LDS (the staging area is reused) and
+  //    store. Lane l, register r of tile tt holds output row 4(l/16) + r,
+  //    column 16(t0 + tt) + l%16.
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int tt = 0; tt < TPW; ++tt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((w * TPW + tt) * 4 + r) * 64 + lane] = acc[tt][r];
+  __syncthreads();
+  for (int o = threadIdx.x; o < TPW * 256; o += NTH) {
+    float v = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < WAVES; ++ww) v += red[ww * TPW * 256 + o];
+    const int ol = o & 63, r = (o >> 6) & 3, tt = o >> 8;
+    const int row = 4 * (ol >> 4) + r;
+    const int cc = 16 * (t0 + tt) + (ol & 15);
+    if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Streamed variant
+// ---------------------------------------------------------------------------
+
+template <int MT, int GPT>
+struct Bundle {
+  u4 wq;                                // one 16-byte slice of the tile: 4 words
+  u4 xa[MT][4];                         // A operand per 32-row block and 16-row tile
+  uint32_t s[GroupsPerBand<GPT>::NG];   // scale bits per group entry
+  uint32_t zw[GroupsPerBand<GPT>::NG];  // packed zero-point word per group entry
+};
+
+struct StreamCtx {
   rsrc_t rx, rs, rz;
-  const u4* qcol;       // first 16-byte slice of this lane in the column tile
+  const u4* qcol;       // this lane's slice of its column tile in band 0
+  int64_t band;         // u4 stride between bands
   uint32_t xoff[4];     // per 16-row tile: byte offset of (row, 8h) or kOOB
   uint32_t soff, zoff;  // byte offsets of this lane's scale / zero word, or kOOB
   uint32_t srow, zrow;  // bytes per group row of scales / zeros
-  int tpg;              // 128-row tiles per group (GPT == 0)
+  int tpg;
 };
 
 template <int MT, int GPT>
-__device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const DecodeCtx& c, int kt) {
-  b.wq = c.qcol[(int64_t)kt * 64];
-  constexpr int NG = GPT > 0 ? GPT : 1;
+__device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const StreamCtx& c, int kt) {
+  using GB = GroupsPerBand<GPT>;
+  b.wq = load_weights(c.qcol + kt * c.band);
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const uint32_t g = GPT == 0 ? (uint32_t)kt / (uint32_t)c.tpg : (uint32_t)(kt * GPT + gi);
+  for (int gi = 0; gi < GB::NG; ++gi) {
+    const uint32_t g = GB::group(kt, gi, c.tpg);
     b.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, c.soff + g * c.srow, 0, 0);
     b.zw[gi] = __builtin_amdgcn_raw_buffer_load_b32(c.rz, c.zoff + g * c.zrow, 0, 0);
   }
@@ -77,47 +328,49 @@ __device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const DecodeCtx&
 }
 
 template <int MT, int GPT>
-__device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT>& b, f4 (&acc)[MT], int col, float valid) {
-  constexpr int NG = GPT > 0 ? GPT : 1;
-  constexpr int JPG = 4 / NG;  // 32-row blocks per group inside the tile
+__device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT>& b, f4 (&acc)[MT], int col, float valid,
+                                               const DecodeConsts& kc) {
+  using GB = GroupsPerBand<GPT>;
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
+  for (int gi = 0; gi < GB::NG; ++gi) {
     const ZeroConst zc = zero_const(zero_nibble(b.zw[gi], col));
     f4 accg[MT];
 #pragma unroll
-    for (int jj = 0; jj < JPG; ++jj) {
-      const int j = gi * JPG + jj;
-      const h8 bw = decode_diff(b.wq[j], zc);
+    for (int jj = 0; jj < GB::JPG; ++jj) {
+      const int j = gi * GB::JPG + jj;
+      const h8 bw = decode_diff_vk(b.wq[j], zc, kc);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
         accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.xa[mt][j]), bw,
                                                           jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg[mt], 0, 0, 0);
     }
-    const float sf = valid * (float)__builtin_bit_cast(_Float16, (uint16_t)b.s[gi]);
+    const float sf = valid * scale_of(b.s[gi]);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] += sf * accg[mt];
   }
 }
 
 template <int MT, int GPT, int WAVES, int DEPTH>
-__global__ __launch_bounds__(64 * WAVES) void decode_kernel(const uint16_t* __restrict__ x,
-                                                            const u4* __restrict__ qw,
-                                                            const uint16_t* __restrict__ scales,
-                                                            const uint32_t* __restrict__ zeros,
-                                                            uint16_t* __restrict__ y, int M, int K, int N, int G,
-                                                            int KT) {
+__global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_t* __restrict__ x,
+                                                                   const u4* __restrict__ qw,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint32_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ y, int M, int K, int N,
+                                                                   int G, int NT) {
   const int t = xcd_remap(blockIdx.x, gridDim.x);
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 4;
   const int col = 16 * t + (lane & 15);
   const int groups = K / G;
+  const int KT = (K + 127) / 128;
 
-  DecodeCtx c;
+  StreamCtx c;
   c.rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   c.rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
   c.rz = make_rsrc(zeros, (uint32_t)groups * (uint32_t)(N / 8) * 4u);
-  c.qcol = qw + (int64_t)t * KT * 64 + lane;
+  c.qcol = qw + (int64_t)t * 64 + lane;
+  c.band = (int64_t)NT * 64;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int row = 16 * mt + (lane & 15);
@@ -128,33 +381,37 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const uint16_t* __re
   c.srow = (uint32_t)N * 2u;
   c.zrow = (uint32_t)(N / 8) * 4u;
   c.tpg = G / 128;
+  const DecodeConsts kc = decode_consts();
 
-  const int KTF = K / 128;  // full 128-row tiles
+  const int KTF = K / 128;
   const int n_my = KTF > w ? (KTF - w + WAVES - 1) / WAVES : 0;
-  const int last = w + WAVES * (n_my - 1);
+  const int last = max(w + WAVES * (n_my - 1), 0);
 
   f4 acc[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  if (n_my > 0) {
-    Bundle<MT, GPT> buf[DEPTH];
+  Bundle<MT, GPT> buf[DEPTH];
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * d, last));
-    const int rounds = (n_my + DEPTH - 1) / DEPTH;
-    for (int r = 0; r < rounds; ++r) {
+  for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * d, last));
+  const int rounds = max((n_my + DEPTH - 1) / DEPTH, 1);
+  for (int r = 0; r < rounds - 1; ++r) {
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) {
-        const int i = r * DEPTH + d;
-        consume_bundle<MT, GPT>(buf[d], acc, col, i < n_my ? 1.f : 0.f);
-        load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * (i + DEPTH), last));
-      }
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i = r * DEPTH + d;
+      consume_bundle<MT, GPT>(buf[d], acc, col, 1.f, kc);
+      load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * (i + DEPTH), last));
     }
   }
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int i = (rounds - 1) * DEPTH + d;
+    consume_bundle<MT, GPT>(buf[d], acc, col, i < n_my ? 1.f : 0.f, kc);
+  }
 
-  // Ragged last tile: rows K .. 128*KT-1 are padding. Its activation loads
-  // are masked per 32-row block; padding blocks also read zero scales and
-  // zero points (their group index is out of range), so they add nothing.
+  // Ragged last band: its activation loads are masked per 32-row block;
+  // padding blocks also read zero scales and zero points (their group index is
+  // out of range), so they add nothing.
   if (KTF < KT && w == (KTF % WAVES)) {
     Bundle<MT, GPT> b;
     load_bundle<MT, GPT>(b, c, KTF);
@@ -164,7 +421,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const uint16_t* __re
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         if (j >= valid_blocks) b.xa[mt][j] = u4{0u, 0u, 0u, 0u};
-    consume_bundle<MT, GPT>(b, acc, col, 1.f);
+    consume_bundle<MT, GPT>(b, acc, col, 1.f, kc);
   }
 
   // Sum the waves' partial tiles. Lane l, register r of 16-row tile mt holds
@@ -198,39 +455,132 @@ __global__ __launch_bounds__(64 * WAVES) void decode_kernel(const uint16_t* __re
   }
 }
 
-template <int MT, int GPT, int WAVES>
-static hipError_t launch_decode_t(const LinearArgs& a, const Launch& L) {
-  constexpr int DEPTH = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
-  const int KT = (a.K + 127) / 128;
+// ---------------------------------------------------------------------------
+// Host side
+// ---------------------------------------------------------------------------
+
+namespace {
+
+constexpr int kStagedDepth = 4;
+
+struct StagedSizes {
+  StagedLayout lay;
+  size_t lds;
+  int S;  // staging iterations per thread (power of two, <= 8; 0 = too many)
+};
+
+StagedSizes staged_sizes(int M, int K, int G, int waves, int tpw) {
+  StagedSizes z;
+  const int nth = 64 * waves;
+  const uint32_t kp = (uint32_t)(K < 128 ? 128 : K);
+  z.lay.x_chunks = kp / 8 + 1;  // one extra 16-byte chunk of padding per row
+  z.lay.x_row = z.lay.x_chunks * 16;
+  z.lay.meta_off = (uint32_t)M * z.lay.x_row;
+  const uint32_t meta_bytes = (uint32_t)(tpw * (K / G) * 16) * 4u;
+  z.lay.scratch_off = (z.lay.meta_off + meta_bytes + 15u) / 16u * 16u;
+  const size_t lds = z.lay.scratch_off + (size_t)nth * 16;
+  const size_t red = (size_t)waves * tpw * 256 * 4;
+  z.lds = lds > red ? lds : red;
+  const int64_t items = std::max<int64_t>((int64_t)M * z.lay.x_chunks, (int64_t)tpw * (K / G) * 16);
+  const int64_t per = (items + nth - 1) / nth;
+  z.S = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
+  return z;
+}
+
+template <typename F>
+hipError_t allow_lds(F kernel, size_t lds) {
+  if (lds <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)lds);
+}
+
+template <int TPW, int GPT, int WAVES, int S>
+hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
   const int NT = (a.N + 15) / 16;
-  return launch_kernel(decode_kernel<MT, GPT, WAVES, DEPTH>, dim3((unsigned)NT), dim3(64 * WAVES), L, a.x,
-                       reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, KT);
+  auto k = decode_staged_kernel<TPW, GPT, WAVES, kStagedDepth, S>;
+  hipError_t e = allow_lds(k, z.lds);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((NT + TPW - 1) / TPW);
+  return launch_kernel(k, dim3(grid), dim3(64 * WAVES), z.lds, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales,
+                       a.zeros, a.y, a.M, a.K, a.N, a.G, NT, z.lay);
+}
+
+template <int TPW, int GPT, int WAVES>
+hipError_t launch_staged_w(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
+  switch (z.S) {
+    case 1: return launch_staged_s<TPW, GPT, WAVES, 1>(a, z, L);
+    case 2: return launch_staged_s<TPW, GPT, WAVES, 2>(a, z, L);
+    case 4: return launch_staged_s<TPW, GPT, WAVES, 4>(a, z, L);
+    case 8: return launch_staged_s<TPW, GPT, WAVES, 8>(a, z, L);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int TPW, int GPT>
+hipError_t launch_staged_g(const LinearArgs& a, int waves, const StagedSizes& z, const Launch& L) {
+  switch (waves) {
+    case 2: return launch_staged_w<TPW, GPT, 2>(a, z, L);
+    case 4: return launch_staged_w<TPW, GPT, 4>(a, z, L);
+    case 8: return launch_staged_w<TPW, GPT, 8>(a, z, L);
+    case 16: return launch_staged_w<TPW, GPT, 16>(a, z, L);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int TPW>
+hipError_t launch_staged_t(const LinearArgs& a, int waves, const StagedSizes& z, const Launch& L) {
+  if (a.G == 32) return launch_staged_g<TPW, 4>(a, waves, z, L);
+  if (a.G == 64) return launch_staged_g<TPW, 2>(a, waves, z, L);
+  if (a.G == 128) return launch_staged_g<TPW, 1>(a, waves, z, L);
+  return launch_staged_g<TPW, 0>(a, waves, z, L);
+}
+
+template <int MT, int GPT, int WAVES>
+hipError_t launch_stream_t(const LinearArgs& a, const Launch& L) {
+  constexpr int DEPTH = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+  const int NT = (a.N + 15) / 16;
+  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, DEPTH>, dim3((unsigned)NT), dim3(64 * WAVES), 0, L, a.x,
+                       reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, NT);
 }
 
 template <int MT, int GPT>
-static hipError_t launch_decode_w(const LinearArgs& a, int waves, const Launch& L) {
+hipError_t launch_stream_w(const LinearArgs& a, int waves, const Launch& L) {
   switch (waves) {
-    case 1: return launch_decode_t<MT, GPT, 1>(a, L);
-    case 2: return launch_decode_t<MT, GPT, 2>(a, L);
-    case 4: return launch_decode_t<MT, GPT, 4>(a, L);
-    case 8: return launch_decode_t<MT, GPT, 8>(a, L);
-    case 16: return launch_decode_t<MT, GPT, 16>(a, L);
+    case 1: return launch_stream_t<MT, GPT, 1>(a, L);
+    case 2: return launch_stream_t<MT, GPT, 2>(a, L);
+    case 4: return launch_stream_t<MT, GPT, 4>(a, L);
+    case 8: return launch_stream_t<MT, GPT, 8>(a, L);
+    case 16: return launch_stream_t<MT, GPT, 16>(a, L);
   }
   return hipErrorInvalidValue;
 }
 
 template <int MT>
-static hipError_t launch_decode_g(const LinearArgs& a, int waves, const Launch& L) {
-  if (a.G == 32) return launch_decode_w<MT, 4>(a, waves, L);
-  if (a.G == 64) return launch_decode_w<MT, 2>(a, waves, L);
-  if (a.G == 128) return launch_decode_w<MT, 1>(a, waves, L);
-  return launch_decode_w<MT, 0>(a, waves, L);
+hipError_t launch_stream_g(const LinearArgs& a, int waves, const Launch& L) {
+  if (a.G == 32) return launch_stream_w<MT, 4>(a, waves, L);
+  if (a.G == 64) return launch_stream_w<MT, 2>(a, waves, L);
+  if (a.G == 128) return launch_stream_w<MT, 1>(a, waves, L);
+  return launch_stream_w<MT, 0>(a, waves, L);
 }
 
-hipError_t launch_decode(const LinearArgs& a, int waves, const Launch& L) {
-  if (a.M <= 16) return launch_decode_g<1>(a, waves, L);
-  if (a.M <= 32) return launch_decode_g<2>(a, waves, L);
-  if (a.M <= 64) return launch_decode_g<4>(a, waves, L);
+}  // namespace
+
+bool decode_staged_fits(int M, int K, int G, int waves, int tpw) {
+  if (M > 16 || waves < 2 || (tpw != 1 && tpw != 2)) return false;
+  const StagedSizes z = staged_sizes(M, K, G, waves, tpw);
+  return z.S > 0 && z.lds <= (size_t)kDecodeLdsBytes;
+}
+
+hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L) {
+  if (cfg.staged) {
+    if (!decode_staged_fits(a.M, a.K, a.G, cfg.waves, cfg.tpw)) return hipErrorInvalidValue;
+    const StagedSizes z = staged_sizes(a.M, a.K, a.G, cfg.waves, cfg.tpw);
+    if (cfg.tpw == 2) return launch_staged_t<2>(a, cfg.waves, z, L);
+    return launch_staged_t<1>(a, cfg.waves, z, L);
+  }
+  if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, L);
+  if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, L);
+  if (a.M <= 64) return launch_stream_g<4>(a, cfg.waves, L);
   return hipErrorInvalidValue;
 }
 

@@ -34,17 +34,26 @@ struct Launch {
 };
 
 template <typename F, typename... Args>
-hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, const Launch& L, Args... args) {
+hipError_t launch_kernel(F kernel, dim3 grid, dim3 block, size_t lds, const Launch& L, Args... args) {
   if (L.start || L.stop)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, L.stream, L.start, L.stop, 0, args...);
+    hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, L.stream, L.start, L.stop, 0, args...);
   else
-    hipLaunchKernelGGL(kernel, grid, block, 0, L.stream, args...);
+    hipLaunchKernelGGL(kernel, grid, block, lds, L.stream, args...);
   return hipGetLastError();
 }
 
-// Decode path: one 16-column tile per workgroup, `waves` waves splitting its
-// K range and summing through LDS.
-hipError_t launch_decode(const LinearArgs& a, int waves, const Launch& L);
+// Decode path. Staged: activations and per-(group, column) scale/zero words
+// are copied to LDS once per workgroup (M <= 16, fits kDecodeLdsBytes), each
+// workgroup owns `tpw` 16-column tiles. Streamed: they are read per tile.
+// Either way `waves` waves split the K range and are summed through LDS.
+constexpr int64_t kDecodeLdsBytes = 160 * 1024;
+struct DecodeConfig {
+  int waves;
+  int tpw;
+  bool staged;
+};
+bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
+hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L);
 
 // Prefill path: LDS-tiled dequantise-then-MFMA GEMM.
 hipError_t launch_prefill(const LinearArgs& a, const Launch& L);

@@ -32,7 +32,7 @@ __device__ __forceinline__ TileCoord tile_coord(int64_t tid, int Npad, int KT) {
   const int kt = (int)(r / 4);
   c.n = n;
   c.k0 = 128 * kt + 32 * j + 8 * h;
-  c.word = ((int64_t)(n / 16) * KT + kt) * 256 + 4 * (16 * h + (n % 16)) + j;
+  c.word = ((int64_t)kt * (Npad / 16) + n / 16) * 256 + 4 * (16 * h + (n % 16)) + j;
   return c;
 }
 

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(const uint16_t* __restrict
       const int t = n0 / 16 + 4 * wn + nt;
       const int col = 16 * t + (lane & 15);
       u4 v = {0u, 0u, 0u, 0u};
-      if (t < NT) v = qw[((int64_t)t * KT + kt) * 64 + lane];
+      if (t < NT) v = qw[((int64_t)kt * NT + t) * 64 + lane];
       wq[nt] = v;
 #pragma unroll
       for (int gi = 0; gi < GPT; ++gi) {
@@ -131,12 +131,12 @@ hipError_t launch_prefill(const LinearArgs& a, const Launch& L) {
   const dim3 grid((unsigned)(n_mtiles * n_ntiles));
   const u4* qw = reinterpret_cast<const u4*>(a.qw);
   if (a.G == 32)
-    return launch_kernel(prefill_kernel<4>, grid, dim3(256), L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G,
+    return launch_kernel(prefill_kernel<4>, grid, dim3(256), 0, L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G,
                          KT, NT, n_mtiles);
   if (a.G == 64)
-    return launch_kernel(prefill_kernel<2>, grid, dim3(256), L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G,
+    return launch_kernel(prefill_kernel<2>, grid, dim3(256), 0, L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G,
                          KT, NT, n_mtiles);
-  return launch_kernel(prefill_kernel<1>, grid, dim3(256), L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, KT,
+  return launch_kernel(prefill_kernel<1>, grid, dim3(256), 0, L, a.x, qw, a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, KT,
                        NT, n_mtiles);
 }
 
