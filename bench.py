@@ -201,9 +201,10 @@ def cpu_baseline(workload, seconds):
     }
 
 
-def traffic_entry(kernel, bytes_alg):
-    """HBM traffic per launch from committed rocprofv3 counter summaries, if
-    they were taken on the current kernel source; else None."""
+def traffic_entry(kernel, shape):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the counters'
+    reading of a plain copy of known size) from the committed rocprofv3
+    summary, if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_traffic.json")
     if not os.path.exists(path):
         return None
@@ -211,7 +212,8 @@ def traffic_entry(kernel, bytes_alg):
         t = json.load(f)
     if t.get("kernel_source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
-    return t.get("hbm_bytes_per_launch")
+    entry = t.get("shapes", {}).get(shape)
+    return round(entry["hbm_bytes_per_launch"]) if entry else None
 
 
 def main():
@@ -306,7 +308,7 @@ def main():
     achieved = alg_bytes / (d["avg_us"] / 1e6) / 1e9
     roofline = {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry("decode", alg_bytes),
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry("decode", dom),
         "kernel": f"decode_kernel ({dom}: K={d['K']} N={d['N']} M={M})", "alg_bytes_per_launch": alg_bytes,
         "avg_launch_us": d["avg_us"],
     }
