@@ -114,6 +114,8 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
  *            of the workgroup's columns staged in LDS once per workgroup
  *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,
  *            scales and zero points read per tile.
+ *   tile:    prefill path: workgroup tile 1 = 128x128 (4 waves),
+ *            2 = 128x256 (8 waves), 3 = 256x256 (8 waves) outputs.
  */
 typedef struct awq_plan {
   int32_t path;
@@ -121,7 +123,8 @@ typedef struct awq_plan {
   int32_t waves;
   int32_t tpw;
   int32_t x_stage;
-  int32_t reserved[3];
+  int32_t tile;
+  int32_t reserved[2];
 } awq_plan;
 
 /* Resolves the automatic fields of *plan for this shape (plan may be all-zero). */

@@ -59,14 +59,17 @@ def test_decode_path(awq, M, K, N, G):
 
 
 @pytest.mark.parametrize("M,K,N,G", [(1, 128, 16, 128), (65, 256, 136, 128), (130, 384, 40, 64),
-                                     (200, 96, 264, 32), (128, 1024, 128, 128), (257, 640, 72, 128)])
+                                     (200, 96, 264, 32), (128, 1024, 128, 128), (257, 640, 72, 128),
+                                     (300, 1024, 520, 256), (513, 640, 264, 128), (96, 160, 24, 32)])
 def test_prefill_path(awq, M, K, N, G):
     log(f"prefill M={M} K={K} N={N} G={G}")
     q, z, s = synth.layer(K, N, G, seed=M + K + 1)
     x = synth.activations(M, K, seed=N + 1)
     y64 = oracle.linear64(x, q, z, s, G)
     D = oracle.l1_scale(x, q, z, s, G)
-    check_close(run(awq, x, q, z, s, G, {"path": 2}), y64, D, what="prefill")
+    for tile in (0, 1, 2, 3):
+        log(f"  tile {tile}")
+        check_close(run(awq, x, q, z, s, G, {"path": 2, "tile": tile}), y64, D, what=f"prefill tile {tile}")
 
 
 def _exact_case(M, K, N, G, seed=0):
@@ -84,7 +87,7 @@ def _exact_case(M, K, N, G, seed=0):
 @pytest.mark.parametrize("plan", [{"path": 1}, {"path": 1, "waves": 16, "x_stage": 1, "tpw": 2},
                                   {"path": 1, "waves": 2, "x_stage": 1, "tpw": 1},
                                   {"path": 1, "waves": 1, "x_stage": 2}, {"path": 1, "waves": 4, "x_stage": 2},
-                                  {"path": 2}])
+                                  {"path": 2, "tile": 1}, {"path": 2, "tile": 2}, {"path": 2, "tile": 3}])
 def test_exact_case_bitwise(awq, plan):
     M, K, N, G = 9, 768, 72, 128
     log(f"exact M={M} K={K} N={N} plan={plan}")

@@ -37,7 +37,7 @@ class AWQError(RuntimeError):
 
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int32), ("split_k", ctypes.c_int32), ("waves", ctypes.c_int32),
-                ("tpw", ctypes.c_int32), ("x_stage", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+                ("tpw", ctypes.c_int32), ("x_stage", ctypes.c_int32), ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 _lib = None
@@ -137,6 +137,7 @@ def _plan(plan):
     p.waves = int(plan.get("waves", 0))
     p.tpw = int(plan.get("tpw", 0))
     p.x_stage = int(plan.get("x_stage", 0))
+    p.tile = int(plan.get("tile", 0))
     return p
 
 
@@ -191,7 +192,7 @@ def dequant(qweight, scales, zeros, K: int, N: int, group: int = 128):
 def linear_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
     p = _plan(plan) or Plan()
     _check(library().awq_linear_plan(M, K, N, group, ctypes.byref(p)))
-    return {"path": p.path, "split_k": p.split_k, "waves": p.waves, "tpw": p.tpw, "x_stage": p.x_stage}
+    return {"path": p.path, "split_k": p.split_k, "waves": p.waves, "tpw": p.tpw, "x_stage": p.x_stage, "tile": p.tile}
 
 
 def linear_workspace_bytes(M: int, K: int, N: int, group: int = 128, plan=None) -> int:

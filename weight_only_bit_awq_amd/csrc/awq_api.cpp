@@ -39,7 +39,7 @@ int check_layer(int64_t K, int64_t N, int G) {
 }
 
 struct Resolved {
-  int path, split, waves, tpw, x_stage;
+  int path, split, waves, tpw, x_stage, tile;
   size_t ws_bytes;
   size_t counter_bytes;
 };
@@ -49,7 +49,8 @@ constexpr int kDecodeMaxM = 64;
 int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out) {
   awq_plan p = {};
   if (in) p = *in;
-  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2)
+  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2 ||
+      p.tile < 0 || p.tile > 3)
     return AWQ_ERR_PLAN;
   if (p.path == 0) p.path = (M <= kDecodeMaxM) ? 1 : 2;
   if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
@@ -60,6 +61,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
   out->waves = 0;
   out->tpw = 0;
   out->x_stage = 0;
+  out->tile = 0;
   out->ws_bytes = 0;
   out->counter_bytes = 0;
   if (p.path == 1) {
@@ -84,11 +86,14 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (x_stage == 1 && !fits) return AWQ_ERR_PLAN;
     if (x_stage == 2) tpw = 1;
     if (x_stage == 2 && p.tpw > 1) return AWQ_ERR_PLAN;
+    if (p.tile) return AWQ_ERR_PLAN;
     out->waves = waves;
     out->tpw = tpw;
     out->x_stage = x_stage;
   } else {
     if (p.split_k > 1 || p.waves || p.tpw || p.x_stage) return AWQ_ERR_PLAN;
+    if (!awq::prefill_fits((int)K, (int)N)) return AWQ_ERR_SHAPE;
+    out->tile = p.tile ? p.tile : awq::prefill_auto_tile((int)M, (int)N);
   }
   return AWQ_OK;
 }
@@ -173,6 +178,7 @@ int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) 
   plan->waves = r.waves;
   plan->tpw = r.tpw;
   plan->x_stage = r.x_stage;
+  plan->tile = r.tile;
   return AWQ_OK;
 }
 
@@ -222,7 +228,7 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
     const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1};
     return hip_status(awq::launch_decode(a, cfg, L));
   }
-  return hip_status(awq::launch_prefill(a, L));
+  return hip_status(awq::launch_prefill(a, r.tile, L));
 }
 
 int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

@@ -88,6 +88,56 @@ __device__ __forceinline__ h2 splat_h2(uint16_t bits) {
   return as_h2((uint32_t)bits | ((uint32_t)bits << 16));
 }
 
+// (a & m) | o with m and o held in VGPRs (see decode_consts): the compiler
+// then selects one v_and_or_b32 (gfx9 VOP3 encodes no literal operands; with
+// literal masks it emits a separate AND and OR).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) { return (a & m) | o; }
+
+struct DecodeConsts {
+  uint32_t m1, m2, o1, o2;  // 0x000F000F, 0x00F000F0, 0x64006400, 0x54005400 in VGPRs
+};
+
+__device__ __forceinline__ DecodeConsts decode_consts() {
+  DecodeConsts k;
+  k.m1 = 0x000F000Fu;
+  k.m2 = 0x00F000F0u;
+  k.o1 = 0x64006400u;
+  k.o2 = 0x54005400u;
+  // opaque to the optimiser: keeps the constants in VGPRs
+  asm volatile("" : "+v"(k.m1), "+v"(k.m2), "+v"(k.o1), "+v"(k.o2));
+  return k;
+}
+
+// Eight rows (q - z) of one device word, exact, as fp16.
+__device__ __forceinline__ h8 decode_diff_vk(uint32_t w, ZeroConst c, const DecodeConsts& k) {
+  const uint32_t w8 = w >> 8;
+  const h2 p0 = as_h2(and_or(w, k.m1, k.o1)) + as_h2(c.c1024);
+  const h2 p1 = as_h2(and_or(w, k.m2, k.o2)) + as_h2(c.c64);
+  const h2 p2 = as_h2(and_or(w8, k.m1, k.o1)) + as_h2(c.c1024);
+  const h2 p3 = as_h2(and_or(w8, k.m2, k.o2)) + as_h2(c.c64);
+  h8 r;
+  r[0] = p0[0]; r[1] = p0[1];
+  r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1];
+  r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Eight dequantised rows fp16((q - z) * s) of one device word.
+__device__ __forceinline__ h8 decode_weight_vk(uint32_t w, ZeroConst c, h2 s2, const DecodeConsts& k) {
+  const uint32_t w8 = w >> 8;
+  const h2 p0 = (as_h2(and_or(w, k.m1, k.o1)) + as_h2(c.c1024)) * s2;
+  const h2 p1 = (as_h2(and_or(w, k.m2, k.o2)) + as_h2(c.c64)) * s2;
+  const h2 p2 = (as_h2(and_or(w8, k.m1, k.o1)) + as_h2(c.c1024)) * s2;
+  const h2 p3 = (as_h2(and_or(w8, k.m2, k.o2)) + as_h2(c.c64)) * s2;
+  h8 r;
+  r[0] = p0[0]; r[1] = p0[1];
+  r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1];
+  r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
 // Zero point of column n from packed zeros row (words of 8 nibbles along N).
 __device__ __forceinline__ uint32_t zero_nibble(uint32_t word, int n) {
   return (word >> (4 * (n & 7))) & 0xFu;

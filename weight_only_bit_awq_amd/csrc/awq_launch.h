@@ -55,7 +55,10 @@ struct DecodeConfig {
 bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L);
 
-// Prefill path: LDS-tiled dequantise-then-MFMA GEMM.
-hipError_t launch_prefill(const LinearArgs& a, const Launch& L);
+// Prefill path: dequantise-then-MFMA GEMM; `tile` selects the workgroup tile
+// (1 = 128x128, 2 = 128x256, 3 = 256x256 outputs).
+int prefill_auto_tile(int M, int N);
+bool prefill_fits(int K, int N);
+hipError_t launch_prefill(const LinearArgs& a, int tile, const Launch& L);
 
 }  // namespace awq
