@@ -114,8 +114,9 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
  *            of the workgroup's columns staged in LDS once per workgroup
  *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,
  *            scales and zero points read per tile.
- *   tile:    prefill path: workgroup tile 1 = 128x128 (4 waves),
- *            2 = 128x256 (8 waves), 3 = 256x256 (8 waves) outputs.
+ *   tile:    prefill path: workgroup tile 1 = 128x128 outputs (4 waves,
+ *            64-row K steps, smallest LDS), 2 = 128x128 (4 waves, 128-row
+ *            steps), 3 = 256x256 (8 waves, 128-row steps).
  */
 typedef struct awq_plan {
   int32_t path;

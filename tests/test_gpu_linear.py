@@ -60,7 +60,8 @@ def test_decode_path(awq, M, K, N, G):
 
 @pytest.mark.parametrize("M,K,N,G", [(1, 128, 16, 128), (65, 256, 136, 128), (130, 384, 40, 64),
                                      (200, 96, 264, 32), (128, 1024, 128, 128), (257, 640, 72, 128),
-                                     (300, 1024, 520, 256), (513, 640, 264, 128), (96, 160, 24, 32)])
+                                     (300, 1024, 520, 256), (513, 640, 264, 128), (96, 160, 24, 32),
+                                     (150, 192, 264, 64), (260, 4160, 48, 64)])
 def test_prefill_path(awq, M, K, N, G):
     log(f"prefill M={M} K={K} N={N} G={G}")
     q, z, s = synth.layer(K, N, G, seed=M + K + 1)

@@ -65,6 +65,19 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
+def _check_no_undefined_kernels(lib: str) -> None:
+    """The host pass of hipcc can drop a kernel's launch stub without an error
+    (a diagnostic it defers inside a template); the library then links but
+    cannot be loaded. Catch that here, naming the missing symbols."""
+    nm = shutil.which("nm") or shutil.which("llvm-nm") or "/opt/rocm/llvm/bin/llvm-nm"
+    res = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"nm failed on {lib}:\n{res.stderr}")
+    missing = [l.split()[-1] for l in res.stdout.splitlines() if "_ZN3awq" in l]
+    if missing:
+        raise RuntimeError("library has undefined kernel symbols (host stub not emitted):\n" + "\n".join(missing))
+
+
 def build(verbose: bool = False, jobs: int = 4) -> str:
     """Compile every source for gfx950 and link ``libawq_mi355x.so`` next to
     this file. Always recompiles. Returns the library path."""
@@ -78,6 +91,7 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"linking {LIB_NAME} failed:\n{res.stdout}\n{res.stderr}")
+    _check_no_undefined_kernels(tmp)
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

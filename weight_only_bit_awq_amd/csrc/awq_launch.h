@@ -56,7 +56,8 @@ bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L);
 
 // Prefill path: dequantise-then-MFMA GEMM; `tile` selects the workgroup tile
-// (1 = 128x128, 2 = 128x256, 3 = 256x256 outputs).
+// (1 = 128x128 with 64-row K steps, 2 = 128x128 with 128-row steps,
+// 3 = 256x256 with 128-row steps).
 int prefill_auto_tile(int M, int N);
 bool prefill_fits(int K, int N);
 hipError_t launch_prefill(const LinearArgs& a, int tile, const Launch& L);
