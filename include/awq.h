@@ -104,7 +104,14 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
  * Execution plan of awq_linear. Zero fields mean "choose automatically".
  *   path:    1 = decode path (dequantise in registers, MFMA 16x16x32, M <= 64),
  *            2 = prefill path (LDS-tiled dequant-then-MFMA GEMM, any M).
- *   split_k: 0 or 1 (reserved for a cross-workgroup K split; not used).
+ *   split_k: prefill path: number of contiguous K ranges (1..16) computed
+ *            by separate workgroups; their fp32 partial sums go to the
+ *            workspace and a second kernel adds them in a fixed order and
+ *            rounds once to fp16 (results do not depend on scheduling).
+ *            Chosen automatically when the output has fewer tiles than the
+ *            chip has workgroup slots (e.g. 512 x 5120 outputs). Must be 0
+ *            or 1 on the decode path, which splits K over the waves of a
+ *            workgroup instead.
  *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
  *            the K range of the workgroup's 16 columns and their partial sums
  *            are added through LDS in a fixed order.
@@ -132,10 +139,11 @@ typedef struct awq_plan {
 int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
 
 /*
- * Workspace bytes awq_linear needs for this shape and plan (0 if none;
- * every current plan needs none). A workspace, when one is needed, must be
- * zero-filled once after allocation, and calls that overlap in time must not
- * share it.
+ * Workspace bytes awq_linear needs for this shape and plan: 0, or
+ * split_k * M * N * 4 bytes of fp32 partial sums for a prefill plan with
+ * split_k > 1. The workspace needs no initialisation (every byte used is
+ * written before it is read); it must be 16-byte aligned, and calls that
+ * overlap in time must not share it.
  */
 int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes);
 int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group,

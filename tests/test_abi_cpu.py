@@ -96,12 +96,20 @@ def test_validation_errors_before_launch(lib):
     p = awq.Plan()
     p.path, p.x_stage = 1, 1  # staged activations need M <= 16
     assert lib.awq_linear_plan(32, 4096, 4096, 128, ctypes.byref(p)) == -7
-    # no cross-workgroup split-K on either path
+    # no cross-workgroup split-K on the decode path
     p = awq.Plan()
     p.path, p.split_k = 1, 4
     need = ctypes.c_size_t(0)
     assert lib.awq_linear_workspace_bytes_ex(1, 4096, 4096, 128, ctypes.byref(p), ctypes.byref(need)) == -7
     assert lib.awq_linear_ex(fake, fake, fake, fake, 1, 4096, 4096, 128, fake, None, 0, ctypes.byref(p), None) == -7
+    # prefill split-K: at most 16; a split plan without its workspace is refused before any launch
+    p = awq.Plan()
+    p.path, p.split_k = 2, 17
+    assert lib.awq_linear_plan(512, 5120, 5120, 128, ctypes.byref(p)) == -7
+    p = awq.Plan()
+    p.path, p.split_k = 2, 4
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 512, 5120, 5120, 128, fake, None, 0, ctypes.byref(p), None) == -5
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 512, 5120, 5120, 128, fake, fake, 16, ctypes.byref(p), None) == -5
 
 
 def test_plans(lib):
@@ -113,9 +121,16 @@ def test_plans(lib):
     assert awq.linear_plan(64, 4096, 4096, 128)["path"] == 1
     assert awq.linear_plan(65, 4096, 4096, 128)["path"] == 2
     assert awq.linear_plan(2048, 5120, 15360, 128)["path"] == 2
-    # no plan needs a workspace
+    # decode plans and well-filled prefill plans need no workspace
     assert awq.linear_workspace_bytes(1, 4096, 12288, 128, {"path": 1, "split_k": 1}) == 0
     assert awq.linear_workspace_bytes(2048, 5120, 15360, 128) == 0
+    # a prefill layer with few output tiles is split over K: fp32 partials per split
+    p512 = awq.linear_plan(512, 5120, 5120, 128)
+    assert p512["path"] == 2 and p512["split_k"] > 1
+    assert awq.linear_workspace_bytes(512, 5120, 5120, 128) == p512["split_k"] * 512 * 5120 * 4
+    assert awq.linear_workspace_bytes(512, 5120, 5120, 128, {"path": 2, "tile": 2, "split_k": 3}) == 3 * 512 * 5120 * 4
+    # never more splits than K steps (a 256-row layer has two 128-row steps)
+    assert awq.linear_plan(512, 256, 5120, 128, {"path": 2, "tile": 2, "split_k": 8})["split_k"] == 2
 
 
 def test_missing_library_raises(tmp_path, monkeypatch):

@@ -73,6 +73,21 @@ def test_prefill_path(awq, M, K, N, G):
         check_close(run(awq, x, q, z, s, G, {"path": 2, "tile": tile}), y64, D, what=f"prefill tile {tile}")
 
 
+@pytest.mark.parametrize("M,K,N,G", [(130, 1024, 40, 128), (300, 2560, 264, 64), (96, 4160, 24, 32),
+                                     (513, 2304, 136, 256)])
+def test_prefill_split_k(awq, M, K, N, G):
+    log(f"prefill split-K M={M} K={K} N={N} G={G}")
+    q, z, s = synth.layer(K, N, G, seed=M + K + 2)
+    x = synth.activations(M, K, seed=N + 2)
+    y64 = oracle.linear64(x, q, z, s, G)
+    D = oracle.l1_scale(x, q, z, s, G)
+    for tile in (1, 2, 3):
+        for split in (2, 3, 5):
+            plan = {"path": 2, "tile": tile, "split_k": split}
+            log(f"  plan {plan} -> {awq.linear_plan(M, K, N, G, plan)}")
+            check_close(run(awq, x, q, z, s, G, plan), y64, D, what=f"{plan}")
+
+
 def _exact_case(M, K, N, G, seed=0):
     rng = np.random.default_rng(seed)
     q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
@@ -88,7 +103,8 @@ def _exact_case(M, K, N, G, seed=0):
 @pytest.mark.parametrize("plan", [{"path": 1}, {"path": 1, "waves": 16, "x_stage": 1, "tpw": 2},
                                   {"path": 1, "waves": 2, "x_stage": 1, "tpw": 1},
                                   {"path": 1, "waves": 1, "x_stage": 2}, {"path": 1, "waves": 4, "x_stage": 2},
-                                  {"path": 2, "tile": 1}, {"path": 2, "tile": 2}, {"path": 2, "tile": 3}])
+                                  {"path": 2, "tile": 1}, {"path": 2, "tile": 2}, {"path": 2, "tile": 3},
+                                  {"path": 2, "tile": 2, "split_k": 3}, {"path": 2, "tile": 3, "split_k": 5}])
 def test_exact_case_bitwise(awq, plan):
     M, K, N, G = 9, 768, 72, 128
     log(f"exact M={M} K={K} N={N} plan={plan}")
@@ -153,5 +169,8 @@ def test_k_zero_and_errors(awq):
     xx = torch.zeros((1, 256), dtype=torch.float16, device="cuda")
     with pytest.raises(awq.AWQError):
         awq.linear(xx, qw, sd, zw, 16, 128, plan={"path": 1, "split_k": 4})
+    with pytest.raises(awq.AWQError):  # split plan, workspace too small
+        awq.linear(torch.zeros((80, 256), dtype=torch.float16, device="cuda"), qw, sd, zw, 16, 128,
+                   workspace=torch.zeros(64, dtype=torch.uint8, device="cuda"), plan={"path": 2, "split_k": 2})
     with pytest.raises(awq.AWQError):
         awq.linear(xx, qw, sd, zw, 16, 128, plan={"path": 1, "waves": 32})

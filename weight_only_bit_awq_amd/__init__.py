@@ -204,8 +204,8 @@ def linear_workspace_bytes(M: int, K: int, N: int, group: int = 128, plan=None) 
 
 
 class Workspace:
-    """A zero-filled device buffer reused across calls on one stream (the
-    library leaves its counters at zero after every call)."""
+    """A device buffer reused across calls on one stream (fp32 partial sums of
+    split-K prefill plans; the library writes every byte it reads)."""
 
     def __init__(self, device=None):
         self.device = device
@@ -216,7 +216,7 @@ class Workspace:
         if nbytes == 0:
             return None
         if self.buf is None or self.buf.numel() < nbytes:
-            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=self.device)
         return self.buf
 
 

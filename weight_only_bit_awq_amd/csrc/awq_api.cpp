@@ -91,9 +91,17 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     out->tpw = tpw;
     out->x_stage = x_stage;
   } else {
-    if (p.split_k > 1 || p.waves || p.tpw || p.x_stage) return AWQ_ERR_PLAN;
+    if (p.waves || p.tpw || p.x_stage) return AWQ_ERR_PLAN;
     if (!awq::prefill_fits((int)K, (int)N)) return AWQ_ERR_SHAPE;
-    out->tile = p.tile ? p.tile : awq::prefill_auto_tile((int)M, (int)N);
+    // K split over workgroups: at most one split per K step, at most 16.
+    if (p.split_k > 16) return AWQ_ERR_PLAN;
+    int tile = p.tile, split = p.split_k;
+    awq::prefill_auto_plan((int)M, (int)K, (int)N, &tile, &split);
+    out->tile = tile;
+    const int steps = awq::prefill_steps((int)K, out->tile);
+    if (split > steps) split = steps > 0 ? steps : 1;
+    out->split = split;
+    out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, split);
   }
   return AWQ_OK;
 }
@@ -220,15 +228,15 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
     if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return AWQ_ERR_ALIGN;
   }
-  if (r.path == 1 && (M * K * 2 >= ((int64_t)1 << 31) || (K / group) * N * 2 >= ((int64_t)1 << 31)))
-    return AWQ_ERR_SHAPE;  // the decode path addresses x and scales with 32-bit buffer offsets
+  if (M * K * 2 >= ((int64_t)1 << 31) || (K / group) * N * 2 >= ((int64_t)1 << 31))
+    return AWQ_ERR_SHAPE;  // the kernels address x and scales with 32-bit buffer offsets
   awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
   const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
   if (r.path == 1) {
     const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1};
     return hip_status(awq::launch_decode(a, cfg, L));
   }
-  return hip_status(awq::launch_prefill(a, r.tile, L));
+  return hip_status(awq::launch_prefill(a, r.tile, r.split, static_cast<float*>(workspace), L));
 }
 
 int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

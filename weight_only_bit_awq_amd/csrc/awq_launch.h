@@ -57,9 +57,14 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
 
 // Prefill path: dequantise-then-MFMA GEMM; `tile` selects the workgroup tile
 // (1 = 128x128 with 64-row K steps, 2 = 128x128 with 128-row steps,
-// 3 = 256x256 with 128-row steps).
-int prefill_auto_tile(int M, int N);
+// 3 = 256x256 with 128-row steps). With splits > 1 the K steps are divided
+// into that many contiguous ranges whose fp32 partials go to `ws`
+// (prefill_workspace_bytes) and are summed by a second kernel.
+int prefill_steps(int K, int tile);
+// Fills *tile and/or *splits where they are 0, from a cost model.
+void prefill_auto_plan(int M, int K, int N, int* tile, int* splits);
+size_t prefill_workspace_bytes(int M, int N, int splits);
 bool prefill_fits(int K, int N);
-hipError_t launch_prefill(const LinearArgs& a, int tile, const Launch& L);
+hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, const Launch& L);
 
 }  // namespace awq

@@ -26,6 +26,13 @@
 //     layout, so these reads are contiguous.
 //   * One barrier per step; out-of-range rows, columns and K read zero (the
 //     loads' out-of-range lanes write zeros to LDS) and are never stored.
+//   * Split-K (for layers with fewer output tiles than the chip has
+//     workgroup slots): workgroup (split, tile) covers a contiguous range of
+//     K steps and writes fp32 partial sums to ws[split][M][N]; a second
+//     kernel adds the splits in a fixed order and rounds once to fp16, so the
+//     result does not depend on scheduling.
+#include <cmath>
+
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -93,16 +100,19 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
                                                                const uint32_t* __restrict__ qw,
                                                                const uint16_t* __restrict__ scales,
                                                                const uint32_t* __restrict__ zeros,
-                                                               uint16_t* __restrict__ y, int M, int K, int N, int G,
-                                                               int NT, int n_mtiles, uint32_t qw_bytes) {
+                                                               uint16_t* __restrict__ y, float* __restrict__ ws, int M,
+                                                               int K, int N, int G, int NT, int n_mtiles, int n_tiles,
+                                                               int split_steps, uint32_t qw_bytes) {
   using C = PrefillCfg<WM, WN, MTW, NTW, KS, GS>;
   using WW = WeightWords<C::KB>;
   typedef typename WW::T wvec;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int u = xcd_remap(blockIdx.x, gridDim.x);
-  const int mtile = u % n_mtiles;
-  const int ntile = u / n_mtiles;
+  const int split = u / n_tiles;
+  const int tile = u - split * n_tiles;
+  const int mtile = tile % n_mtiles;
+  const int ntile = tile / n_mtiles;
   const int m0 = mtile * C::BM;
   const int n0 = ntile * C::BN;
   const int tid = threadIdx.x;
@@ -112,6 +122,8 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   const int h = lane >> 4;
   const int groups = K / G;
   const int nsteps = (K + KS - 1) / KS;
+  const int step0 = split * split_steps;                   // this workgroup's K steps:
+  const int step1 = min(nsteps, step0 + split_steps);      // [step0, step1), never empty
 
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const rsrc_t rq = make_rsrc(qw, qw_bytes);
@@ -173,13 +185,13 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
     for (int b = 0; b < NTW; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
   wvec cb[NTW], rb[NTW];
-  issue_stage(0, 0);
-  load_b(0, cb);
+  issue_stage(step0, 0);
+  load_b(step0, cb);
 
   const DecodeConsts kc = decode_consts();
   const int arow0 = 16 * MTW * wm + (lane & 15);
   const int ccol0 = 16 * NTW * wn + (lane & 15);  // column within the workgroup tile, nt = 0
-  for (int step = 0; step < nsteps; ++step) {
+  for (int step = step0; step < step1; ++step) {
     // Wait for this wave's loads of the current stage, then for everyone's;
     // the barrier also frees the other buffer (read during the last step).
     // The wait is explicit: the compiler does not count loads that write LDS
@@ -187,12 +199,12 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
     // of them), and an explicit s_waitcnt is never relaxed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool more = step + 1 < nsteps;
+    const bool more = step + 1 < step1;
     if (more) {
       load_b(step + 1, rb);
-      issue_stage(step + 1, (step + 1) & 1);
+      issue_stage(step + 1, (step + 1 - step0) & 1);
     }
-    const char* st = smem + (step & 1) * C::STAGE;
+    const char* st = smem + ((step - step0) & 1) * C::STAGE;
     const uint16_t* sc_l = reinterpret_cast<const uint16_t*>(st + C::SC_OFF);
     const uint32_t* zw_l = reinterpret_cast<const uint32_t*>(st + C::ZW_OFF);
     ZeroConst zc[NTW];
@@ -237,20 +249,43 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 16 * (MTW * wm + mt) + 4 * h + r;
         const float v = acc[mt][nt][r];
-        if (row < M && col < N) y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        if (row < M && col < N) {
+          if (ws)
+            ws[((int64_t)split * M + row) * N + col] = v;
+          else
+            y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
       }
     }
+}
+
+// y = fp16(sum over s of ws[s]), s in increasing order; four elements per thread.
+__global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __restrict__ ws, uint16_t* __restrict__ y,
+                                                             int64_t mn, int splits) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= mn) return;
+  f4 a = *reinterpret_cast<const f4*>(ws + i);
+  for (int s = 1; s < splits; ++s) a += *reinterpret_cast<const f4*>(ws + (int64_t)s * mn + i);
+  typedef uint16_t us4 __attribute__((ext_vector_type(4)));
+  us4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(uint16_t, (_Float16)a[e]);
+  *reinterpret_cast<us4*>(y + i) = o;
 }
 
 namespace {
 
 template <int WM, int WN, int MTW, int NTW, int KS, int GS>
-hipError_t launch_prefill_t(const LinearArgs& a, const Launch& L) {
+hipError_t launch_prefill_t(const LinearArgs& a, int splits, float* ws, const Launch& L) {
   using C = PrefillCfg<WM, WN, MTW, NTW, KS, GS>;
   const int NT = (a.N + 15) / 16;
   const int KT = (a.K + 127) / 128;
   const int n_mtiles = (a.M + C::BM - 1) / C::BM;
   const int n_ntiles = (a.N + C::BN - 1) / C::BN;
+  const int nsteps = (a.K + KS - 1) / KS;
+  // Steps per split rounded so that every split is non-empty.
+  const int split_steps = (nsteps + splits - 1) / splits;
+  splits = (nsteps + split_steps - 1) / split_steps;
   auto k = prefill_kernel<WM, WN, MTW, NTW, KS, GS>;
   if (C::LDS_BYTES > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -258,41 +293,105 @@ hipError_t launch_prefill_t(const LinearArgs& a, const Launch& L) {
     if (e != hipSuccess) return e;
   }
   const uint32_t qw_bytes = (uint32_t)((size_t)NT * KT * 1024);
-  return launch_kernel(k, dim3((unsigned)(n_mtiles * n_ntiles)), dim3(C::NTH), C::LDS_BYTES, L, a.x, a.qw,
-                       a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, NT, n_mtiles, qw_bytes);
+  const int n_tiles = n_mtiles * n_ntiles;
+  float* part = splits > 1 ? ws : nullptr;
+  const Launch first{L.stream, L.start, part ? nullptr : L.stop};
+  hipError_t e = launch_kernel(k, dim3((unsigned)(n_tiles * splits)), dim3(C::NTH), C::LDS_BYTES, first, a.x, a.qw,
+                               a.scales, a.zeros, a.y, part, a.M, a.K, a.N, a.G, NT, n_mtiles, n_tiles, split_steps,
+                               qw_bytes);
+  if (e != hipSuccess || !part) return e;
+  const int64_t mn = (int64_t)a.M * a.N;
+  const Launch second{L.stream, nullptr, L.stop};
+  return launch_kernel(prefill_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, second, part, a.y,
+                       mn, splits);
 }
 
 // Groups per step: KS / G for G < KS, else 1 (G is then a multiple of KS).
 template <int WM, int WN, int MTW, int NTW, int KS>
-hipError_t launch_prefill_k(const LinearArgs& a, const Launch& L) {
+hipError_t launch_prefill_k(const LinearArgs& a, int splits, float* ws, const Launch& L) {
   if (a.G < KS) {
-    if (KS / a.G == 2) return launch_prefill_t<WM, WN, MTW, NTW, KS, 2>(a, L);
-    if (KS == 128 && a.G == 32) return launch_prefill_t<WM, WN, MTW, NTW, KS, (KS == 128 ? 4 : 2)>(a, L);
+    if (KS / a.G == 2) return launch_prefill_t<WM, WN, MTW, NTW, KS, 2>(a, splits, ws, L);
+    if (KS == 128 && a.G == 32) return launch_prefill_t<WM, WN, MTW, NTW, KS, (KS == 128 ? 4 : 2)>(a, splits, ws, L);
     return hipErrorInvalidValue;
   }
-  return launch_prefill_t<WM, WN, MTW, NTW, KS, 1>(a, L);
+  return launch_prefill_t<WM, WN, MTW, NTW, KS, 1>(a, splits, ws, L);
 }
 
 }  // namespace
 
-int prefill_auto_tile(int M, int N) {
-  // The 256 x 256 tile halves the activation and weight re-reads of the
-  // 128 x 128 ones and does half the redundant decoding per MFMA, but holds a
-  // CU with one workgroup: measured on the LLaMA-shaped layers it wins from
-  // about 150 tiles up (160 tiles on 256 CUs already beat 640 small ones);
-  // below that the 128 x 128 tile with 128-row steps is best.
-  const long t3 = (long)((M + 255) / 256) * ((N + 255) / 256);
-  return t3 >= 150 ? 3 : 2;
+int prefill_steps(int K, int tile) { return (K + (tile == 1 ? 63 : 127)) / (tile == 1 ? 64 : 128); }
+
+namespace {
+
+// Estimated time of a prefill plan, from a model fitted to measurements on
+// the LLaMA-shaped layers (MI355X): the workgroups run in rounds of
+// `slots` (resident workgroups per chip), each round takes one workgroup's
+// K range, and the split-K partials cost a write and a read of fp32 per
+// output per split. Times in microseconds.
+double prefill_cost(int M, int K, int N, int tile, int splits) {
+  const int bm = tile == 3 ? 256 : 128, bn = tile == 3 ? 256 : 128;
+  const double tiles = (double)((M + bm - 1) / bm) * (double)((N + bn - 1) / bn);
+  const int steps = prefill_steps(K, tile);
+  const double wgs = tiles * splits;
+  double slots, t_step;  // t_step: one K step of one workgroup
+  if (tile == 3) {
+    slots = 256, t_step = 3.8;
+  } else if (tile == 2) {
+    slots = 512, t_step = wgs <= 256 ? 1.6 : 2.8;  // alone on its CU, or sharing it
+  } else {
+    slots = 768, t_step = 1.9;
+  }
+  const double rounds = std::ceil(wgs / slots);
+  const double per_wg = std::ceil((double)steps / splits) * t_step;
+  const double reduce = splits > 1 ? 1.4e-6 * splits * (double)M * (double)N : 0.0;
+  return rounds * per_wg + reduce;
+}
+
+int best_split(int M, int K, int N, int tile, double* cost) {
+  const int steps = prefill_steps(K, tile);
+  int best = 1;
+  double bc = prefill_cost(M, K, N, tile, 1);
+  for (int s = 2; s <= 8 && s * 4 <= steps; ++s) {
+    const double c = prefill_cost(M, K, N, tile, s);
+    if (c < bc) bc = c, best = s;
+  }
+  if (cost) *cost = bc;
+  return best;
+}
+
+}  // namespace
+
+void prefill_auto_plan(int M, int K, int N, int* tile, int* splits) {
+  // A fixed tile gets its best split; a fixed split its best tile; else both.
+  if (*tile && !*splits) {
+    *splits = best_split(M, K, N, *tile, nullptr);
+    return;
+  }
+  double bc = 0;
+  int bt = 0, bs = 1;
+  for (int t = 2; t <= 3; ++t) {
+    double c;
+    int s = *splits ? *splits : best_split(M, K, N, t, &c);
+    if (*splits) c = prefill_cost(M, K, N, t, s);
+    if (!bt || c < bc) bc = c, bt = t, bs = s;
+  }
+  if (!*tile) *tile = bt;
+  if (!*splits) *splits = bs;
+}
+
+size_t prefill_workspace_bytes(int M, int N, int splits) {
+  return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 bool prefill_fits(int K, int N) { return (size_t)((N + 15) / 16) * ((K + 127) / 128) * 1024 < ((size_t)1 << 31); }
 
-hipError_t launch_prefill(const LinearArgs& a, int tile, const Launch& L) {
+hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, const Launch& L) {
   if (!prefill_fits(a.K, a.N)) return hipErrorInvalidValue;
+  if (splits > 1 && !ws) return hipErrorInvalidValue;
   switch (tile) {
-    case 1: return launch_prefill_k<2, 2, 4, 4, 64>(a, L);   // 128 x 128, 4 waves of 64 x 64, 64-row steps
-    case 2: return launch_prefill_k<2, 2, 4, 4, 128>(a, L);  // 128 x 128, 4 waves of 64 x 64, 128-row steps
-    case 3: return launch_prefill_k<2, 4, 8, 4, 128>(a, L);  // 256 x 256, 8 waves of 128 x 64
+    case 1: return launch_prefill_k<2, 2, 4, 4, 64>(a, splits, ws, L);   // 128 x 128, 4 waves of 64 x 64, 64-row steps
+    case 2: return launch_prefill_k<2, 2, 4, 4, 128>(a, splits, ws, L);  // 128 x 128, 4 waves of 64 x 64, 128-row steps
+    case 3: return launch_prefill_k<2, 4, 8, 4, 128>(a, splits, ws, L);  // 256 x 256, 8 waves of 128 x 64, 128-row steps
   }
   return hipErrorInvalidValue;
 }
