@@ -226,7 +226,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
-    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
@@ -333,21 +333,26 @@ def main():
                     if L.K == K:
                         L.x[:, cols] *= 20
                         break
+            per_kernel_times(lib, torch, hip, play, 5)  # warm-up: first launches, clocks
             pt = per_kernel_times(lib, torch, hip, play, args.prefill_reps)
             tot_flop, tot_ms = 0.0, 0.0
             for name, L in play:
-                avg = sum(pt[name]) / len(pt[name])
+                ts = sorted(pt[name])
+                med = ts[len(ts) // 2]
                 fl = 2.0 * Mp * L.K * L.N
                 tot_flop += fl
-                tot_ms += avg
-                prefill["shapes"][f"{name}@M={Mp}"] = {"K": L.K, "N": L.N, "avg_us": round(avg * 1e3, 2),
-                                                        "TFLOPs": round(fl / (avg / 1e3) / 1e12, 1)}
+                tot_ms += med
+                prefill["shapes"][f"{name}@M={Mp}"] = {
+                    "K": L.K, "N": L.N, "median_us": round(med * 1e3, 2),
+                    "p10_us": round(ts[len(ts) // 10] * 1e3, 2), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 2),
+                    "TFLOPs": round(fl / (med / 1e3) / 1e12, 1),
+                    "plan": awq.linear_plan(Mp, L.K, L.N, 128)}
             prefill[f"M={Mp}"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
             del play
             torch.cuda.empty_cache()
         prefill["value"] = prefill["M=2048"]
         big = max((k for k in prefill["shapes"] if k.endswith("M=2048")),
-                  key=lambda k: prefill["shapes"][k]["avg_us"])
+                  key=lambda k: prefill["shapes"][k]["median_us"])
         pv = prefill["shapes"][big]["TFLOPs"]
         prefill["roofline"] = {"bound": "mfma", "achieved": pv, "peak": FP16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
                                "frac": round(pv / FP16_DENSE_PEAK_TFLOPS, 4), "traffic": None,

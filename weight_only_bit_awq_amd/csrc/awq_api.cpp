@@ -72,14 +72,14 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (p.waves && p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8 && p.waves != 16)
       return AWQ_ERR_PLAN;
     if (p.tpw > 2) return AWQ_ERR_PLAN;
-    // Automatic choice (measured on the LLaMA-shaped decode layers): about
-    // 2048 waves over the 256 CUs, four waves per workgroup for wide layers
-    // and eight for narrow ones; two column tiles per workgroup when that
-    // still leaves at least two workgroups per CU.
+    // Automatic choice (measured on the LLaMA-shaped decode layers, M = 1):
+    // one 16-column tile per workgroup and eight waves splitting K, unless
+    // that makes more than about 12k waves (very wide layers: four), or the
+    // layer has fewer than 8 full 128-row bands.
     int waves = p.waves;
-    if (!waves) waves = (NT * 4 >= 2048 || KT < 32) ? 4 : 8;
+    if (!waves) waves = (NT * 8 > 12288 || KT < 8) ? 4 : 8;
     int tpw = p.tpw;
-    if (!tpw) tpw = (NT >= 1024) ? 2 : 1;
+    if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
     const bool fits = M >= 1 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
     if (x_stage == 0) x_stage = fits ? 1 : 2;

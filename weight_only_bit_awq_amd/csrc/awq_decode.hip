@@ -23,12 +23,13 @@
 //   * Per word: 1 shift, 4 mask-and-or (v_and_or_b32), 4 packed fp16
 //     subtractions give the exact (q - z) as fp16. The per-group scale is
 //     applied once per group to the fp32 MFMA result.
-//   * Staged variant (M <= 16 and the data fits in LDS): at the start each
-//     workgroup copies the activation rows and, for its columns, one 32-bit
-//     word per (group, column) holding the scale bits and the zero point
-//     into LDS. The loop then issues exactly one global load per tile, DEPTH
-//     tiles ahead, and reads the A operand and the group word from LDS (LDS
-//     reads have their own counter and never wait on the weight stream).
+//   * Staged variant (M <= 16 and the activations fit in LDS): at the start
+//     each workgroup copies the activation rows into LDS; the loop reads the
+//     A operand from there. Each band's scale and packed zero word are loaded
+//     into registers right before the band's weights, DEPTH bands ahead, so
+//     they arrive in order with the weights (measured: staging them up front
+//     made every workgroup wait several microseconds for them behind the
+//     whole chip's weight stream).
 //   * Streamed variant (larger M or K): activations, scales and zero points
 //     are read per tile with raw buffer loads.
 //   * Rows >= M and columns >= N read as zero (out-of-range buffer offsets) or
@@ -72,8 +73,16 @@ __device__ __forceinline__ float scale_of(uint32_t bits) {
 struct StagedLayout {
   uint32_t x_row;        // bytes per staged activation row (K padded to >= 128, + 16)
   uint32_t x_chunks;     // 16-byte chunks per staged row
-  uint32_t meta_off;     // byte offset of the group words
   uint32_t scratch_off;  // per-thread 16-byte slots for masked staging stores
+};
+
+// Weights of one band for TPW column tiles and their groups' scale bits and
+// packed zero words (lane l: column l % 16 of each tile).
+template <int TPW, int NG>
+struct BandBuf {
+  u4 wq[TPW];
+  uint32_t s[TPW][NG];
+  uint32_t zw[TPW][NG];
 };
 
 template <int TPW, int GPT, int WAVES, int DEPTH, int S>
@@ -100,43 +109,55 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   const rsrc_t rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
   const rsrc_t rz = make_rsrc(zeros, (uint32_t)groups * (uint32_t)(N / 8) * 4u);
 
-  // 1. Staging loads (activations and group words), issued first: they come
-  //    from L2 and are waited for before the weight stream is.
+  // 1. Staging loads (activations), issued first: they come from L2 and are
+  //    waited for before the weight stream is.
   const uint32_t x_total = (uint32_t)M * lay.x_chunks;
-  const uint32_t m_total = (uint32_t)(TPW * groups * 16);
   u4 xv[S];
-  uint32_t sv[S], zv[S];
 #pragma unroll
   for (int i = 0; i < S; ++i) {
     const uint32_t e = threadIdx.x + i * NTH;
     const uint32_t row = e / lay.x_chunks, cc = e - row * lay.x_chunks;
     const bool ok = e < x_total && cc * 8u < (uint32_t)K;
     xv[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (row * K + cc * 8u) * 2u : kOOB, 0, 0));
-    const uint32_t tt = e / (uint32_t)(groups * 16), rem = e - tt * (uint32_t)(groups * 16);
-    const uint32_t g = rem >> 4, col = 16u * (t0 + tt) + (rem & 15u);
-    // Offsets are below 2^31, so setting bit 31 makes a masked load read
-    // zero (written as arithmetic: a select here becomes a branch).
-    const uint32_t bad = (uint32_t)!(e < m_total && col < (uint32_t)N) << 31;
-    sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, ((g * N + col) * 2u) | bad, 0, 0);
-    zv[i] = __builtin_amdgcn_raw_buffer_load_b32(rz, ((g * (N / 8) + (col >> 3)) * 4u) | bad, 0, 0);
-    zv[i] = (zv[i] >> (4 * (col & 7))) & 0xFu;
   }
 
-  // 2. Weight prefetch: one 16-byte load per lane per tile, DEPTH bands ahead.
-  //    The index is clamped to the wave's last band (band 0 when it has none,
-  //    which always exists), so the prefetch is unconditional and the waits
-  //    before the staging stores cover only the staging loads.
+  // 2. Weight prefetch: per band, the scale and zero word of each of the
+  //    lane's columns, then one 16-byte load per lane per tile, DEPTH bands
+  //    ahead. The band index is clamped to the wave's last band (band 0 when
+  //    it has none, which always exists), so the prefetch is unconditional
+  //    and the waits before the staging stores cover only the staging loads.
+  //    Offsets are below 2^31, so setting bit 31 makes a masked load read
+  //    zero; group indices are clamped to the last group (a ragged band's
+  //    missing groups are then never used with nonzero weight).
   const int n_my = KTF > w ? (KTF - w + WAVES - 1) / WAVES : 0;
   const int last = max(w + WAVES * (n_my - 1), 0);
   const u4* qcol[TPW];
+  uint32_t soff[TPW], zoff[TPW];
 #pragma unroll
-  for (int tt = 0; tt < TPW; ++tt) qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
+  for (int tt = 0; tt < TPW; ++tt) {
+    qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
+    const uint32_t col = 16u * (t0 + tt) + (lane & 15u);
+    const uint32_t bad = (uint32_t)!(col < (uint32_t)N) << 31;
+    soff[tt] = (col * 2u) | bad;
+    zoff[tt] = ((col >> 3) * 4u) | bad;
+  }
   const int64_t band = (int64_t)NT * 64;
-  u4 buf[DEPTH][TPW];
+  const uint32_t srow = (uint32_t)N * 2u, zrow = (uint32_t)(N / 8) * 4u;
+  auto load_band = [&](BandBuf<TPW, GB::NG>& b, int kt) {
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
+    for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) buf[d][tt] = load_weights(qcol[tt] + min(w + WAVES * d, last) * band);
+      for (int gi = 0; gi < GB::NG; ++gi) {
+        const uint32_t g = min(GB::group(kt, gi, tpg), (uint32_t)groups - 1u);
+        b.s[tt][gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[tt] + g * srow, 0, 0);
+        b.zw[tt][gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[tt] + g * zrow, 0, 0);
+      }
+      b.wq[tt] = load_weights(qcol[tt] + kt * band);
+    }
+  };
+  BandBuf<TPW, GB::NG> buf[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) load_band(buf[d], min(w + WAVES * d, last));
 
   // 3. Staging stores (masked ones go to this thread's scratch slot) and barrier.
 #pragma unroll
@@ -145,8 +166,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
     const uint32_t row = e / lay.x_chunks, cc = e - row * lay.x_chunks;
     const uint32_t xa = e < x_total ? row * lay.x_row + cc * 16u : lay.scratch_off + threadIdx.x * 16u;
     *reinterpret_cast<u4*>(smem + xa) = xv[i];
-    const uint32_t ma = e < m_total ? lay.meta_off + e * 4u : lay.scratch_off + threadIdx.x * 16u;
-    *reinterpret_cast<uint32_t*>(smem + ma) = sv[i] | (zv[i] << 16);
   }
   __syncthreads();
 
@@ -154,12 +173,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   const DecodeConsts kc = decode_consts();
   const int rowc = min(lane & 15, M - 1);  // rows >= M read row M-1; never stored
   const char* xrow = smem + rowc * lay.x_row + 16 * h;
-  const char* meta = smem + lay.meta_off + (lane & 15) * 4;
   f4 acc[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) acc[tt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  auto consume = [&](const u4 (&wq)[TPW], int kt, float valid) {
+  const int lcol = lane & 15;  // column within a tile (16-column tiles start at multiples of 8)
+  auto consume = [&](const BandBuf<TPW, GB::NG>& b, int kt, float valid) {
     h8 a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const h8*>(xrow + 256 * kt + 64 * j);
@@ -167,19 +186,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
     for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
       for (int gi = 0; gi < GB::NG; ++gi) {
-        // clamped: the zero-weighted round of a wave without full bands may
-        // visit a ragged band whose last groups do not exist
-        const uint32_t g = min(GB::group(kt, gi, tpg), (uint32_t)groups - 1u);
-        const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta + ((tt * groups + g) * 16) * 4);
-        const ZeroConst zc = zero_const(mw >> 16);
+        const ZeroConst zc = zero_const(zero_nibble(b.zw[tt][gi], lcol));
         f4 accg;
 #pragma unroll
         for (int jj = 0; jj < GB::JPG; ++jj) {
           const int j = gi * GB::JPG + jj;
-          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], decode_diff_vk(wq[tt][j], zc, kc),
+          accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], decode_diff_vk(b.wq[tt][j], zc, kc),
                                                         jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg, 0, 0, 0);
         }
-        acc[tt] += (valid * scale_of(mw & 0xFFFFu)) * accg;
+        acc[tt] += (valid * scale_of(b.s[tt][gi])) * accg;
       }
     }
   };
@@ -193,9 +208,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
     for (int d = 0; d < DEPTH; ++d) {
       const int i = r * DEPTH + d;
       consume(buf[d], w + WAVES * i, 1.f);
-      const int nk = min(w + WAVES * (i + DEPTH), last);
-#pragma unroll
-      for (int tt = 0; tt < TPW; ++tt) buf[d][tt] = load_weights(qcol[tt] + nk * band);
+      load_band(buf[d], min(w + WAVES * (i + DEPTH), last));
     }
   }
 #pragma unroll
@@ -207,27 +220,24 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   // 5. Ragged last band: blocks past K are skipped; groups past the last one
   //    hold no data and are skipped as well.
   if (KTF < KT && w == (KTF % WAVES)) {
-    u4 wq[TPW];
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt) wq[tt] = load_weights(qcol[tt] + KTF * band);
+    BandBuf<TPW, GB::NG> b;
+    load_band(b, KTF);
     const int valid_blocks = (K - 128 * KTF) / 32;
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
       for (int gi = 0; gi < GB::NG; ++gi) {
         if (gi * GB::JPG >= valid_blocks) continue;
-        const uint32_t g = GB::group(KTF, gi, tpg);
-        const uint32_t mw = *reinterpret_cast<const uint32_t*>(meta + ((tt * groups + g) * 16) * 4);
-        const ZeroConst zc = zero_const(mw >> 16);
+        const ZeroConst zc = zero_const(zero_nibble(b.zw[tt][gi], lcol));
         f4 accg = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int jj = 0; jj < GB::JPG; ++jj) {
           const int j = gi * GB::JPG + jj;
           if (j < valid_blocks)
             accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8*>(xrow + 256 * KTF + 64 * j),
-                                                          decode_diff_vk(wq[tt][j], zc, kc), accg, 0, 0, 0);
+                                                          decode_diff_vk(b.wq[tt][j], zc, kc), accg, 0, 0, 0);
         }
-        acc[tt] += scale_of(mw & 0xFFFFu) * accg;
+        acc[tt] += scale_of(b.s[tt][gi]) * accg;
       }
   }
 
@@ -440,13 +450,11 @@ StagedSizes staged_sizes(int M, int K, int G, int waves, int tpw) {
   const uint32_t kp = (uint32_t)(K < 128 ? 128 : K);
   z.lay.x_chunks = kp / 8 + 1;  // one extra 16-byte chunk of padding per row
   z.lay.x_row = z.lay.x_chunks * 16;
-  z.lay.meta_off = (uint32_t)M * z.lay.x_row;
-  const uint32_t meta_bytes = (uint32_t)(tpw * (K / G) * 16) * 4u;
-  z.lay.scratch_off = (z.lay.meta_off + meta_bytes + 15u) / 16u * 16u;
+  z.lay.scratch_off = (uint32_t)M * z.lay.x_row;
   const size_t lds = z.lay.scratch_off + (size_t)nth * 16;
   const size_t red = (size_t)waves * tpw * 256 * 4;
   z.lds = lds > red ? lds : red;
-  const int64_t items = std::max<int64_t>((int64_t)M * z.lay.x_chunks, (int64_t)tpw * (K / G) * 16);
+  const int64_t items = (int64_t)M * z.lay.x_chunks;
   const int64_t per = (items + nth - 1) / nth;
   z.S = per <= 1 ? 1 : per <= 2 ? 2 : per <= 4 ? 4 : per <= 8 ? 8 : 0;
   return z;
