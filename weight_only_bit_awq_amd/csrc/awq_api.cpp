@@ -81,6 +81,10 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
+    // long K: sixteen waves stage twice as much per pass
+    if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw) &&
+        awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
+      waves = 16;
     const bool fits = M >= 1 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
     if (x_stage == 0) x_stage = fits ? 1 : 2;
     if (x_stage == 1 && !fits) return AWQ_ERR_PLAN;
