@@ -201,6 +201,115 @@ def cpu_baseline(workload, seconds):
     }
 
 
+def _short(name):
+    return name.split("(")[0].replace("void ", "")
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
+    """Turn the CSV output of three rocprofv3 runs of this script (kernel
+    trace; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the last two with
+    --copy-calibration) into profiles/decode_prefill_llama_bench.md and the
+    per-shape traffic files read by traffic_entry().
+
+    Dispatches are matched to layer shapes by their order, which main()
+    fixes: decode calls cycle through the decode workload's shapes; prefill
+    calls come in two equal blocks (M = 512, then 2048), each cycling through
+    the prefill workload's shapes; a split-K reduce kernel belongs to the
+    prefill call it follows."""
+    import csv
+    import statistics
+    import synth
+
+    def rows(d, name):
+        with open(os.path.join(d, name)) as f:
+            return sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+
+    def label(seq):
+        """[(kernel, key, record)] of awq dispatches -> {(path, shape): [[records of one call], ...]}"""
+        dec = [r for r in seq if "decode_" in r[0]]
+        pre = [r for r in seq if "prefill_" in r[0]]
+        out = {}
+        dshapes = [sh.name for sh in synth.LLAMA2_7B_DECODE.shapes]
+        for i, r in enumerate(dec):
+            out.setdefault(("decode", dshapes[i % len(dshapes)]), []).append([r])
+        pw = synth.LLAMA2_13B_PREFILL
+        calls = []
+        for r in pre:
+            if "reduce" in r[0] and calls:
+                calls[-1].append(r)
+            else:
+                calls.append([r])
+        half = len(calls) // 2
+        for i, c in enumerate(calls):
+            Mp = pw.Ms[0] if i < half else pw.Ms[1]
+            sh = pw.shapes[(i if i < half else i - half) % len(pw.shapes)]
+            out.setdefault(("prefill", f"{sh.name}@M={Mp}"), []).append(c)
+        return out
+
+    trace = [(_short(r["Kernel_Name"]), None, r) for r in rows(trace_dir, "bench_kernel_trace.csv")
+             if "awq::" in r["Kernel_Name"]]
+    dur = label(trace)
+
+    def counter_calls(d):
+        rs = rows(d, "bench_counter_collection.csv")
+        copy = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        return label([(_short(r["Kernel_Name"]), None, r) for r in rs if "awq::" in r["Kernel_Name"]]), copy[-1]
+
+    fe, copy_f = counter_calls(fetch_dir)
+    wr, copy_w = counter_calls(write_dir)
+    ff, fw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
+    dshape = {sh.name: sh for sh in synth.LLAMA2_7B_DECODE.shapes}
+    pshape = {sh.name: sh for sh in synth.LLAMA2_13B_PREFILL.shapes}
+
+    def alg_bytes(path, shape):
+        if path == "decode":
+            sh = dshape[shape]
+            return weight_set_bytes(sh.K, sh.N, 128) + 2 * sh.K + 2 * sh.N
+        name, m = shape.split("@M=")
+        sh, Mp = pshape[name], int(m)
+        return weight_set_bytes(sh.K, sh.N, 128) + 2 * Mp * sh.K + 2 * Mp * sh.N
+
+    lines = ["# rocprofv3 summary: W4A16 linear kernels of bench.py on one MI355X", "",
+             "Workloads: LLaMA-2-7B-shaped decode stack (M=1, 32 layers x QKV 4096x12288, O 4096x4096, "
+             "gate+up 4096x22016, down 11008x4096) and LLaMA-2-13B-shaped prefill GEMMs (M=512 and 2048; "
+             "QKV 5120x15360, O 5120x5120, gate+up 5120x27648, down 13824x5120), group 128.", "",
+             "Commands (each run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "The table below comes from `python bench.py --summarize-profiles TRACE FETCH WRITE` on "
+              "their output directories.", "",
+              "Calibration: a plain 1 GiB device copy (`__amd_rocclr_copyBuffer`) reads "
+              f"FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = {copy_w:.1f} KiB, so the per-dispatch counters "
+              f"below are scaled by {ff:.4f} (fetch) and {fw:.4f} (write).", "",
+              "| path | shape | kernels of one call | calls | kernel-trace us (median / min / max) | "
+              "FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    traffic = {"decode": {}, "prefill": {}}
+    for (path, shape), calls in sorted(dur.items()):
+        per_call = [sum((int(r[2]["End_Timestamp"]) - int(r[2]["Start_Timestamp"])) / 1e3 for r in c)
+                    for c in calls]
+        names = " + ".join(f"{r[0]} (grid {r[2]['Grid_Size_X']})" for r in calls[0])
+        f_calls = fe.get((path, shape), [])
+        w_calls = wr.get((path, shape), [])
+        f_kib = statistics.mean(sum(float(r[2]["Counter_Value"]) for r in c) for c in f_calls) if f_calls else 0
+        w_kib = statistics.mean(sum(float(r[2]["Counter_Value"]) for r in c) for c in w_calls) if w_calls else 0
+        hbm = f_kib * 1024 * ff + w_kib * 1024 * fw
+        alg = alg_bytes(path, shape)
+        lines.append(f"| {path} | {shape} | {names} | {len(per_call)} | {statistics.median(per_call):.2f} / "
+                     f"{min(per_call):.2f} / {max(per_call):.2f} | {f_kib:.0f} | {w_kib:.0f} | {hbm / 1e6:.2f} MB | "
+                     f"{alg / 1e6:.2f} MB | {hbm / alg:.3f} |")
+        traffic[path][shape] = {"kernels": names, "read_bytes_per_launch": f_kib * 1024 * ff,
+                                "write_bytes_per_launch": w_kib * 1024 * fw, "hbm_bytes_per_launch": hbm,
+                                "alg_bytes_per_launch": alg, "median_us": statistics.median(per_call)}
+    md = os.path.join(ROOT, "profiles", "decode_prefill_llama_bench.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    for path in ("decode", "prefill"):
+        with open(os.path.join(ROOT, "profiles", f"{path}_traffic.json"), "w") as f:
+            json.dump({"kernel_source_sha": source_sha(KERNEL_SOURCES[path]), "fetch_scale": ff,
+                       "write_scale": fw, "shapes": traffic[path], "source": os.path.basename(md)}, f, indent=1)
+    print("\n".join(lines))
+
+
 def traffic_entry(kernel, shape):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the counters'
     reading of a plain copy of known size) from the committed rocprofv3
@@ -227,9 +336,17 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
+    ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output of this script, then exit")
+    ap.add_argument("--profile-commands", nargs="*", default=[],
+                    help="the rocprofv3 command lines, quoted in the summary")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(*args.summarize_profiles, args.profile_commands)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer's multi-GPU "
@@ -355,8 +472,8 @@ def main():
                   key=lambda k: prefill["shapes"][k]["median_us"])
         pv = prefill["shapes"][big]["TFLOPs"]
         prefill["roofline"] = {"bound": "mfma", "achieved": pv, "peak": FP16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
-                               "frac": round(pv / FP16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
-                               "kernel": f"prefill_kernel ({big})"}
+                               "frac": round(pv / FP16_DENSE_PEAK_TFLOPS, 4),
+                               "traffic": traffic_entry("prefill", big), "kernel": f"prefill_kernel ({big})"}
         eprint(f"[bench] prefill: M=2048 {prefill['M=2048']} TFLOP/s, M=512 {prefill['M=512']} TFLOP/s")
 
     if args.copy_calibration:
