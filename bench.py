@@ -161,6 +161,64 @@ def per_kernel_times(lib, torch, hip, layers, reps):
     return out
 
 
+def stream_read_times(lib, torch, hip, layers, reps):
+    """Plain streaming read (awq_stream_read) of each layer's qweight buffer,
+    cycling through the stack so every read is cold: the achievable HBM read
+    rate at that size. Returns {shape: (bytes, [ms, ...])}."""
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    sink = torch.empty(16, dtype=torch.uint8, device=layers[0][1].qw.device)
+    n = len(layers) * reps
+    evs = hip.create(2 * n)
+    i = 0
+    for _ in range(reps):
+        for name, L in layers:
+            nb = L.qw.numel() * L.qw.element_size()
+            st = lib.awq_stream_read(L.qw.data_ptr(), nb, sink.data_ptr(), stream, evs[2 * i], evs[2 * i + 1])
+            if st:
+                raise RuntimeError(f"awq_stream_read failed: {lib.awq_status_string(st).decode()}")
+            i += 1
+    torch.cuda.synchronize()
+    out = {}
+    i = 0
+    for _ in range(reps):
+        for name, L in layers:
+            nb = L.qw.numel() * L.qw.element_size()
+            out.setdefault(name, (nb, []))[1].append(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]))
+            i += 1
+    return out
+
+
+def fp16_dense_times(torch, shapes, M, dev, reps=20, copies=4):
+    """The same layer shapes as a plain fp16 linear layer (torch's
+    F.linear on a dense fp16 weight in its [N, K] layout, i.e. the vendor
+    BLAS): the W16A16 counterpart of the W4A16 layer. Weights rotate over
+    `copies` copies. Returns {shape: median ms}."""
+    import torch.nn.functional as F
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    out = {}
+    for name, K, N in shapes:
+        x = torch.randn((M, K), device=dev, generator=gen).half()
+        ws = [torch.randn((N, K), device=dev, generator=gen).half() for _ in range(copies)]
+        for w in ws:
+            F.linear(x, w)
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            F.linear(x, ws[r % copies])
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        out[name] = ts[len(ts) // 2]
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(workload, seconds):
     """The fp64 oracle on host cores, on one layer of the stack (M=1),
     repeated until about `seconds` of CPU work; weight GB/s."""
@@ -418,6 +476,15 @@ def main():
             "weight_GBps": round(wb / (avg / 1e3) / 1e9, 1), "alg_GBps": round(alg / (avg / 1e3) / 1e9, 1),
             "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
         }
+    # Context for the roofline: the achievable streaming-read rate at each
+    # layer's size, and the same shapes as dense fp16 weights (W16A16).
+    sr = stream_read_times(lib, torch, hip, layers, args.kernel_reps)
+    for name, (nb, ts) in sr.items():
+        ts = sorted(ts)
+        med = ts[len(ts) // 2]
+        p = per_shape[name]
+        p["stream_read_GBps"] = round(nb / (med / 1e3) / 1e9, 1)
+        p["pct_of_stream_read"] = round(100 * p["weight_GBps"] / p["stream_read_GBps"], 1)
     kern_sum_ms = sum(p["avg_us"] for p in per_shape.values()) * wl.layers / 1e3
     dom = max(per_shape, key=lambda k: per_shape[k]["avg_us"])
     d = per_shape[dom]
@@ -428,15 +495,28 @@ def main():
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_entry("decode", dom),
         "kernel": f"decode_kernel ({dom}: K={d['K']} N={d['N']} M={M})", "alg_bytes_per_launch": alg_bytes,
         "avg_launch_us": d["avg_us"],
+        "stream_read_GBps_same_size": d.get("stream_read_GBps"),
     }
     eprint(f"[bench] per-kernel: " + ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s"
                                                for k, v in per_shape.items()))
 
+    del graph
+    layers = None
+    torch.cuda.empty_cache()
+    fp16 = fp16_dense_times(torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], M, dev)
+    fp16_layer_ms = sum(fp16.values())
+    w4_layer_ms = sum(p["avg_us"] for p in per_shape.values()) / 1e3
+    for name, ms in fp16.items():
+        per_shape[name]["fp16_dense_us"] = round(ms * 1e3, 3)
+        per_shape[name]["speedup_vs_fp16"] = round(ms * 1e3 / per_shape[name]["avg_us"], 3)
+    fp16_ref = {"what": "the same M=1 layer shapes as dense fp16 weights through torch F.linear (vendor BLAS), "
+                        "median event time per call; the W16A16 counterpart of the W4A16 layer",
+                "layer_us": round(fp16_layer_ms * 1e3, 2), "w4a16_layer_us": round(w4_layer_ms * 1e3, 2),
+                "speedup_w4a16_over_fp16": round(fp16_layer_ms / w4_layer_ms, 3)}
+    eprint(f"[bench] fp16 dense layer {fp16_layer_ms * 1e3:.1f} us vs W4A16 {w4_layer_ms * 1e3:.1f} us")
+
     prefill = None
     if not args.no_prefill:
-        del graph
-        layers = None
-        torch.cuda.empty_cache()
         pw = synth.LLAMA2_13B_PREFILL
         prefill = {"metric": "GEMM TFLOP/s at M=2048", "unit": "TFLOP/s", "workload": pw.name, "shapes": {}}
         for Mp in pw.Ms:
@@ -467,6 +547,14 @@ def main():
             prefill[f"M={Mp}"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
             del play
             torch.cuda.empty_cache()
+        dense = fp16_dense_times(torch, [(sh.name, sh.K, sh.N) for sh in pw.shapes], max(pw.Ms), dev, reps=20,
+                                 copies=2)
+        dflop = sum(2.0 * max(pw.Ms) * sh.K * sh.N for sh in pw.shapes)
+        prefill["dense_fp16_torch"] = {
+            "what": "the same M=2048 shapes as a dense fp16 GEMM through torch F.linear (vendor BLAS)",
+            "TFLOPs": round(dflop / (sum(dense.values()) / 1e3) / 1e12, 1),
+            "shapes": {k: round(2.0 * max(pw.Ms) * sh.K * sh.N / (dense[k] / 1e3) / 1e12, 1)
+                       for k, sh in ((s.name, s) for s in pw.shapes)}}
         prefill["value"] = prefill["M=2048"]
         big = max((k for k in prefill["shapes"] if k.endswith("M=2048")),
                   key=lambda k: prefill["shapes"][k]["median_us"])
@@ -509,6 +597,7 @@ def main():
         "kernel_sum_ms_per_step": round(kern_sum_ms, 5),
         "per_kernel": per_shape,
         "roofline": roofline,
+        "fp16_dense_reference": fp16_ref,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

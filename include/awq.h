@@ -167,16 +167,28 @@ int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* sc
 
 /*
  * awq_linear_timed: awq_linear_ex that also records two hipEvent_t handles
- * (passed as void*, either may be NULL) at the start and at the end of the
- * layer's kernel itself (hipExtLaunchKernelGGL), so that hipEventElapsedTime
- * gives the kernel's own duration. Every awq_linear call is one kernel launch
- * (split-K partials are reduced inside that kernel). For measurement only:
- * not for use under stream capture.
+ * (passed as void*, either may be NULL): `start_event` at the start of the
+ * call's first kernel and `stop_event` at the end of its last kernel
+ * (hipExtLaunchKernelGGL), so that hipEventElapsedTime gives the call's own
+ * kernel time. A call is one kernel, or two for a prefill plan with
+ * split_k > 1 (the GEMM, then the fixed-order reduction of its partials).
+ * For measurement only: not for use under stream capture.
  */
 int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                      const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
                      uint16_t* y, void* workspace, size_t workspace_bytes,
                      const awq_plan* plan, void* stream, void* start_event, void* stop_event);
+
+/*
+ * Measurement aid, not part of the layer: a plain streaming read of `bytes`
+ * bytes (a multiple of 16) at device address `buf` (16-byte aligned) with
+ * 16-byte loads, the achievable HBM read rate at that size against which a
+ * weight-streaming launch of the same size is compared. The 16 bytes at
+ * device address `sink` may receive a value derived from the data (it keeps
+ * the loads live). Events as in awq_linear_timed (either may be NULL).
+ */
+int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
+                    void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

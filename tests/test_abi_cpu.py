@@ -139,3 +139,11 @@ def test_missing_library_raises(tmp_path, monkeypatch):
     monkeypatch.setattr(awq, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(awq.AWQLibraryMissing):
         awq.library()
+
+
+def test_stream_read_validates_before_launch(lib):
+    # nothing below reaches a kernel: empty, NULL, size and alignment errors
+    assert lib.awq_stream_read(None, 0, None, None, None, None) == 0
+    assert lib.awq_stream_read(None, 1024, ctypes.c_void_p(4096), None, None, None) == -1
+    assert lib.awq_stream_read(ctypes.c_void_p(4096), 1000, ctypes.c_void_p(4096), None, None, None) == -2
+    assert lib.awq_stream_read(ctypes.c_void_p(4104), 1024, ctypes.c_void_p(4096), None, None, None) == -4

@@ -70,6 +70,8 @@ _SIGS = {
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 

@@ -250,6 +250,15 @@ int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* sc
                           nullptr, nullptr);
 }
 
+int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream, void* start_event, void* stop_event) {
+  if (bytes == 0) return AWQ_OK;
+  if (!buf || !sink) return AWQ_ERR_NULL;
+  if (bytes % 16) return AWQ_ERR_SHAPE;
+  if (!aligned(buf, 16) || !aligned(sink, 16)) return AWQ_ERR_ALIGN;
+  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return hip_status(awq::launch_stream_read(buf, (uint64_t)bytes, sink, L));
+}
+
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
                int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
   return awq_linear_ex(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream);

@@ -67,4 +67,8 @@ size_t prefill_workspace_bytes(int M, int N, int splits);
 bool prefill_fits(int K, int N);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, const Launch& L);
 
+// Plain streaming read of `bytes` (a multiple of 16) at `buf`; the 16 bytes at
+// `sink` may receive a value derived from the data.
+hipError_t launch_stream_read(const void* buf, uint64_t bytes, void* sink, const Launch& L);
+
 }  // namespace awq
