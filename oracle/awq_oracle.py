@@ -272,6 +272,51 @@ def round_output16(y64: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Round-to-nearest group quantiser (fp16 W -> q, z, s)
+# ----------------------------------------------------------------------------
+
+RTN_QMAX = 15  # 2^4 - 1 levels above code 0
+
+
+def quantize_rtn(w: np.ndarray, G: int):
+    """fp16 W [K, N] -> (q uint8 [K, N], z uint8 [K/G, N], s fp16 [K/G, N]).
+
+    The step that makes the "real" INT4 weights before the W4A16 kernel runs
+    (TinyChat README, *Usage*, step 3: ``--w_bit 4 --q_group_size 128``,
+    ``--q_backend real``); the Sagemaker page names the plain variant,
+    round-to-nearest (RTN), in its *GGUF* section. The pages print no formula;
+    the reading taken here is the asymmetric min-max rule, per group of G
+    input channels and per output column:
+
+        lo, hi = min and max of the group's weights
+        s      = fp16((hi - lo) / 15)           (1 if that rounds to 0)
+        z      = clamp(rne(-lo / s), 0, 15)
+        q[k]   = clamp(rne(w[k] / s) + z, 0, 15)
+
+    rne = round half to even. Every operation is one IEEE float32 operation
+    (difference, quotient, conversion), taken in that order: the pages fix no
+    precision, so the integer decisions are made in the kernel's float32 and
+    both sides reach the same codes. The dequantised weight (q - z) * s then
+    lies within s/2 (plus the fp16 rounding of s) of w wherever lo <= 0 <= hi;
+    a group that does not contain 0 has its zero point clamped (z = 0 or 15)
+    and loses the end of its range. Inputs must be finite."""
+    w = np.asarray(w, dtype=np.float16)
+    K, N = w.shape
+    if G <= 0 or K % G:
+        raise ValueError("K must be a positive multiple of the group size")
+    wg = w.reshape(K // G, G, N).astype(np.float32)
+    lo = wg.min(axis=1)
+    hi = wg.max(axis=1)
+    s32 = (hi - lo) / np.float32(RTN_QMAX)
+    s16 = s32.astype(np.float16)
+    s16 = np.where(s16 == 0, np.float16(1.0), s16).astype(np.float16)
+    sf = s16.astype(np.float32)
+    z = np.clip(np.rint(-lo / sf), 0, RTN_QMAX)
+    q = np.clip(np.rint(wg / sf[:, None, :]) + z[:, None, :], 0, RTN_QMAX)
+    return (q.reshape(K, N).astype(np.uint8), z.astype(np.uint8), s16)
+
+
+# ----------------------------------------------------------------------------
 # Byte accounting (the size arithmetic the pages use)
 # ----------------------------------------------------------------------------
 

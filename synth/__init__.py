@@ -114,3 +114,10 @@ FALCON_180B_STACK = Workload(
 
 WORKLOADS = (SINGLE_4096, LLAMA2_7B_DECODE, LLAMA3_8B_SWEEP, LLAMA2_13B_PREFILL,
              FALCON_180B_STACK)
+
+
+def dense_weights(K: int, N: int, seed: int = 0, layer_id: int = 0, std: float = 0.02):
+    """fp16 weights [K, N] ~ N(0, std^2) (the usual initialisation scale of
+    LLM linear layers): input of the round-to-nearest quantiser."""
+    rng = _rng(seed, 3, layer_id, K, N)
+    return (rng.standard_normal(size=(K, N)) * std).astype(np.float16)
