@@ -219,6 +219,37 @@ def fp16_dense_times(torch, shapes, M, dev, reps=20, copies=4):
     return out
 
 
+def quantize_times(awq, torch, shapes, G, dev, reps=10):
+    """awq_quantize (fp16 W -> device qweight, scales, zeros) on each shape;
+    HBM bytes per call = 2 B per weight read + the quantised weight set
+    written. Returns {shape: {...}}."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(77)
+    out = {}
+    for name, K, N in shapes:
+        ws = [(torch.randn((K, N), device=dev, generator=gen) * 0.02).half() for _ in range(2)]
+        for w in ws:
+            awq.quantize(w, G)
+        torch.cuda.synchronize()
+        ts = []
+        for r in range(reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            awq.quantize(ws[r % 2], G)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        med = ts[len(ts) // 2]
+        nbytes = 2 * K * N + weight_set_bytes(K, N, G)
+        out[name] = {"K": K, "N": N, "median_us": round(med * 1e3, 2), "hbm_bytes": nbytes,
+                     "GBps": round(nbytes / (med / 1e3) / 1e9, 1)}
+        del ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(workload, seconds):
     """The fp64 oracle on host cores, on one layer of the stack (M=1),
     repeated until about `seconds` of CPU work; weight GB/s."""
@@ -515,6 +546,16 @@ def main():
                 "speedup_w4a16_over_fp16": round(fp16_layer_ms / w4_layer_ms, 3)}
     eprint(f"[bench] fp16 dense layer {fp16_layer_ms * 1e3:.1f} us vs W4A16 {w4_layer_ms * 1e3:.1f} us")
 
+    qt = quantize_times(awq, torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], wl.G, dev)
+    qdom = max(qt, key=lambda k: qt[k]["median_us"])
+    quantize = {"what": "awq_quantize: round-to-nearest group quantiser, fp16 W [K,N] (N(0, 0.02)) -> device "
+                        "qweight + fp16 scales + packed zero points, on the decode stack's layer shapes",
+                "shapes": qt,
+                "roofline": {"bound": "hbm", "achieved": qt[qdom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                             "frac": round(qt[qdom]["GBps"] / HBM_PEAK_GBS, 4),
+                             "kernel": f"quantize_kernel ({qdom})"}}
+    eprint("[bench] quantize: " + ", ".join(f"{k} {v['median_us']}us {v['GBps']}GB/s" for k, v in qt.items()))
+
     prefill = None
     if not args.no_prefill:
         pw = synth.LLAMA2_13B_PREFILL
@@ -598,6 +639,7 @@ def main():
         "per_kernel": per_shape,
         "roofline": roofline,
         "fp16_dense_reference": fp16_ref,
+        "quantize": quantize,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

@@ -101,6 +101,22 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
                 int64_t K, int64_t N, int group, uint16_t* w, void* stream);
 
 /*
+ * awq_quantize: fp16 weights w [K, N] (16-byte aligned) -> device-layout
+ * qweight (awq_qweight_words words, padding included), fp16 scales
+ * [K/G, N] and packed zero points [K/G, N/8]: the round-to-nearest group
+ * quantiser that makes the "real" INT4 weights (TinyChat README "Usage"
+ * step 3; the plain round-to-nearest variant is named on the Sagemaker
+ * page, section "GGUF"). Per group of G input channels and output column:
+ *     s = fp16((max - min) / 15), or 1 if that rounds to 0,
+ *     z = clamp(rne(-min / s), 0, 15),  q = clamp(rne(w / s) + z, 0, 15),
+ * every step one IEEE float32 operation, rne = round half to even. Weights
+ * must be finite. A group whose range does not contain 0 has its zero point
+ * clamped and loses the far end of its range.
+ */
+int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* qweight,
+                 uint16_t* scales, uint32_t* zeros, void* stream);
+
+/*
  * Execution plan of awq_linear. Zero fields mean "choose automatically".
  *   path:    1 = decode path (dequantise in registers, MFMA 16x16x32, M <= 64),
  *            2 = prefill path (LDS-tiled dequant-then-MFMA GEMM, any M).

@@ -70,6 +70,8 @@ _SIGS = {
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "awq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]),
 }
@@ -191,6 +193,23 @@ def dequant(qweight, scales, zeros, K: int, N: int, group: int = 128):
     return out
 
 
+def quantize(w, group: int = 128):
+    """fp16 w [K, N] -> (qweight device words, scales fp16 [K/G, N], zeros
+    int32 [K/G, N/8]): the round-to-nearest group quantiser."""
+    torch = _torch()
+    _need(w, torch.float16, "w", 2)
+    K, N = w.shape
+    if group <= 0:
+        raise ValueError("group must be positive")
+    # shapes the library rejects (K % group, N % 8) fail in the call below
+    qw = torch.empty(qweight_words(K, N), dtype=torch.int32, device=w.device)
+    scales = torch.empty((K // group, N), dtype=torch.float16, device=w.device)
+    zeros = torch.empty((K // group, N // 8), dtype=torch.int32, device=w.device)
+    _check(library().awq_quantize(w.data_ptr(), K, N, group, qw.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                  _stream(w.device)))
+    return qw, scales, zeros
+
+
 def linear_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
     p = _plan(plan) or Plan()
     _check(library().awq_linear_plan(M, K, N, group, ctypes.byref(p)))
@@ -258,6 +277,6 @@ def linear(x, qweight, scales, zeros, N: int, group: int = 128, out=None, worksp
     return out
 
 
-__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "linear", "linear_plan",
+__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_plan",
            "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",
            "abi_version"]

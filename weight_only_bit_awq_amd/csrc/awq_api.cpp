@@ -178,6 +178,17 @@ int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t*
   return hip_status(awq::launch_dequant(qweight, scales, zeros, (int)K, (int)N, group, w, (hipStream_t)stream));
 }
 
+int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* qweight, uint16_t* scales,
+                 uint32_t* zeros, void* stream) {
+  int st = check_dims(0, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (K == 0 || N == 0) return AWQ_OK;
+  if (!w || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4)) return AWQ_ERR_ALIGN;
+  return hip_status(awq::launch_quantize(w, (int)K, (int)N, group, qweight, scales, zeros, (hipStream_t)stream));
+}
+
 int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) {
   int st = check_dims(M, K, N);
   if (st) return st;

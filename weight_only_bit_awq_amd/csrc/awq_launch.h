@@ -15,6 +15,11 @@ hipError_t launch_dequant(const uint32_t* qw, const uint16_t* scales, const uint
 
 hipError_t launch_fill_zero(uint16_t* y, int64_t n, hipStream_t st);
 
+// Round-to-nearest group quantiser: fp16 w [K, N] -> device qweight, fp16
+// scales [K/G, N], packed zeros [K/G, N/8].
+hipError_t launch_quantize(const uint16_t* w, int K, int N, int G, uint32_t* qw, uint16_t* scales, uint32_t* zeros,
+                           hipStream_t st);
+
 struct LinearArgs {
   const uint16_t* x;
   const uint32_t* qw;
