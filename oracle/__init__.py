@@ -9,4 +9,5 @@ from .awq_oracle import (device_layout_doc, device_words, pack_canonical,  # noq
                          unpack_device, dequant64, dequant16, linear64, linear64_w16,
                          l1_scale, normalised_error, linear_bruteforce, round_output16,
                          weight_set_bytes, model_bytes, low_nibble,
-                         quantize_rtn, RTN_QMAX)
+                         quantize_rtn, RTN_QMAX, silu64, linear_silu_mul64,
+                         silu_mul_scale)

@@ -272,6 +272,45 @@ def round_output16(y64: np.ndarray) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# Gated epilogue: y = silu(gate) * up on a fused gate+up layer
+# ----------------------------------------------------------------------------
+
+
+def silu64(h: np.ndarray) -> np.ndarray:
+    """silu(h) = h * sigmoid(h) = h / (1 + exp(-h)), in float64 (exp of a
+    large positive -h overflows to inf and gives the correct limit 0)."""
+    h = np.asarray(h, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return h / (1.0 + np.exp(-h))
+
+
+def linear_silu_mul64(x, q, z, s, G) -> np.ndarray:
+    """The fused gate+up projection of a gated MLP followed by its gate:
+    h = x . W with W = [W_gate | W_up] (output columns 0 .. N/2-1 are the
+    gate, N/2 .. N-1 the up projection), y[m, i] = silu(h[m, i]) * h[m, N/2+i].
+
+    The pages measure LLaMA-family decoders ("TinyChat" README, *Speed
+    Benchmarks*), whose MLP takes this form, and TinyChat fuses the small
+    operators around its W4A16 kernels; the column order of the fused weight
+    is not printed, so gate-then-up halves are the reading taken here."""
+    h = linear64(x, q, z, s, G)
+    n2 = h.shape[1] // 2
+    return silu64(h[:, :n2]) * h[:, n2:]
+
+
+def silu_mul_scale(x, q, z, s, G) -> np.ndarray:
+    """Error scale of the gated output: 1.1 |u| D_gate + |silu(g)| D_up + |y|,
+    with D the L1 norms of ``l1_scale`` (1.1 bounds |silu'|, so an error
+    e_g in g and e_u in u moves y by at most 1.1 |u| e_g + |silu(g)| e_u);
+    the |y| term covers the final fp16 rounding."""
+    h = linear64(x, q, z, s, G)
+    D = l1_scale(x, q, z, s, G)
+    n2 = h.shape[1] // 2
+    g, u = h[:, :n2], h[:, n2:]
+    return 1.1 * np.abs(u) * D[:, :n2] + np.abs(silu64(g)) * D[:, n2:] + np.abs(silu64(g) * u)
+
+
+# ----------------------------------------------------------------------------
 # Round-to-nearest group quantiser (fp16 W -> q, z, s)
 # ----------------------------------------------------------------------------
 
