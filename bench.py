@@ -161,6 +161,59 @@ def per_kernel_times(lib, torch, hip, layers, reps):
     return out
 
 
+def time_stack_graph(lib, torch, layers, steps, warmup):
+    """Capture one pass over the stack (every launch, in order, on one
+    stream) in a HIP graph and replay it: wall-clock and event ms per step,
+    K steps between two synchronisations."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        s = ctypes.c_void_p(side.cuda_stream)
+        for _, L in layers:
+            L.launch(lib, s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for _, L in layers:
+            L.launch(lib, s)
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del graph
+    return (t1 - t0) * 1e3 / steps, e0.elapsed_time(e1) / steps
+
+
+def per_shape_stats(awq, lib, torch, hip, wl, layers, M, reps):
+    """Per layer shape: kernel durations from events at the kernels' own
+    start and end (eager pass), weight and algorithmic GB/s, the plan."""
+    times = per_kernel_times(lib, torch, hip, layers, reps)
+    per_shape = {}
+    for sh in wl.shapes:
+        ts = sorted(times[sh.name])
+        avg = sum(ts) / len(ts)
+        wb = weight_set_bytes(sh.K, sh.N, wl.G)
+        alg = wb + 2 * M * sh.K + 2 * M * sh.N
+        per_shape[sh.name] = {
+            "K": sh.K, "N": sh.N, "launches": len(ts), "avg_us": round(avg * 1e3, 3),
+            "p10_us": round(ts[len(ts) // 10] * 1e3, 3), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
+            "weight_GBps": round(wb / (avg / 1e3) / 1e9, 1), "alg_GBps": round(alg / (avg / 1e3) / 1e9, 1),
+            "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
+        }
+    return per_shape
+
+
 def stream_read_times(lib, torch, hip, layers, reps):
     """Plain streaming read (awq_stream_read) of each layer's qweight buffer,
     cycling through the stack so every read is cold: the achievable HBM read
@@ -216,6 +269,69 @@ def fp16_dense_times(torch, shapes, M, dev, reps=20, copies=4):
         out[name] = ts[len(ts) // 2]
         del ws
         torch.cuda.empty_cache()
+    return out
+
+
+def gated_times(awq, lib, torch, hip, K, N, G, M, dev, copies, reps):
+    """Fused gate+up with the silu(gate) * up epilogue (awq_linear_silu_mul,
+    events at its kernels' own start and end) against the unfused sequence:
+    awq_linear writing [M, N] fp16, then torch's silu and multiply on the two
+    halves (a graph of 20 repetitions of those two, per repetition). Weights
+    rotate over `copies` layers. Returns medians in microseconds."""
+    import torch.nn.functional as F
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    x = torch.randn((M, K), device=dev, generator=gen).half()
+    h = torch.empty((M, N), dtype=torch.float16, device=dev)
+    yg = torch.empty((M, N // 2), dtype=torch.float16, device=dev)
+    ws = awq.Workspace(dev)
+    layers = [Layer(awq, torch, K, N, G, gen, x, h, ws, dev) for _ in range(copies)]
+    nb = awq.linear_silu_mul_workspace_bytes(M, K, N, G)
+    buf = ws.get(max(nb, awq.linear_workspace_bytes(M, K, N, G)))
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    evs = hip.create(2 * reps * copies)
+    fused, lin, elt = [], [], []
+    for r in range(reps + 1):
+        for i, L in enumerate(layers):
+            e = 2 * ((r % reps) * copies + i)
+            st = lib.awq_linear_silu_mul_ex(x.data_ptr(), L.qw.data_ptr(), L.s.data_ptr(), L.zw.data_ptr(), M, K, N,
+                                            G, yg.data_ptr(), buf.data_ptr() if buf is not None else None,
+                                            buf.numel() if buf is not None else 0, None, stream, evs[e], evs[e + 1])
+            if st:
+                raise RuntimeError(lib.awq_status_string(st).decode())
+        torch.cuda.synchronize()
+        if r:
+            fused += [hip.elapsed_ms(evs[2 * ((r % reps) * copies + i)], evs[2 * ((r % reps) * copies + i) + 1])
+                      for i in range(copies)]
+    lin = per_kernel_times(lib, torch, hip, [("l", L) for L in layers], reps)["l"]
+    # torch's silu and multiply captured in a graph and replayed, so that the
+    # host's launch latency stays out of the per-call time
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        torch.mul(F.silu(h[:, : N // 2]), h[:, N // 2:], out=yg)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(20):
+            torch.mul(F.silu(h[:, : N // 2]), h[:, N // 2:], out=yg)
+    torch.cuda.synchronize()
+    for r in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        elt.append(e0.elapsed_time(e1) / 20)
+    del g
+    med = lambda t: sorted(t)[len(t) // 2] * 1e3
+    out = {"K": K, "N": N, "M": M, "fused_us": round(med(fused), 2), "linear_us": round(med(lin), 2),
+           "torch_silu_mul_us": round(med(elt), 2)}
+    out["unfused_us"] = round(out["linear_us"] + out["torch_silu_mul_us"], 2)
+    out["plan"] = awq.linear_silu_mul_plan(M, K, N, G)
+    del layers
+    torch.cuda.empty_cache()
     return out
 
 
@@ -423,6 +539,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-g64", action="store_true", help="skip the group-64 (Falcon-7B) decode stack")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -459,54 +576,12 @@ def main():
     step_bytes = sum(weight_set_bytes(L.K, L.N, L.G) for _, L in layers)
     eprint(f"[bench] weight set {step_bytes / 1e9:.3f} GB resident")
 
-    # Capture one step (all 128 launches) in a HIP graph.
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        s = ctypes.c_void_p(side.cuda_stream)
-        for _, L in layers:
-            L.launch(lib, s)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for _, L in layers:
-            L.launch(lib, s)
-    torch.cuda.synchronize()
-
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall_ms = (t1 - t0) * 1e3 / args.steps
-    event_ms = e0.elapsed_time(e1) / args.steps
+    wall_ms, event_ms = time_stack_graph(lib, torch, layers, args.steps, args.warmup)
     value = step_bytes / (wall_ms / 1e3) / 1e9
     eprint(f"[bench] decode stack: {wall_ms:.4f} ms/step wall, {event_ms:.4f} ms/step events, {value:.1f} GB/s")
 
     # Per-kernel durations (events at the kernels' own start/end).
-    times = per_kernel_times(lib, torch, hip, layers, args.kernel_reps)
-    per_shape = {}
-    for sh in wl.shapes:
-        ts = sorted(times[sh.name])
-        avg = sum(ts) / len(ts)
-        wb = weight_set_bytes(sh.K, sh.N, wl.G)
-        alg = wb + 2 * M * sh.K + 2 * M * sh.N
-        per_shape[sh.name] = {
-            "K": sh.K, "N": sh.N, "launches": len(ts), "avg_us": round(avg * 1e3, 3),
-            "p10_us": round(ts[len(ts) // 10] * 1e3, 3), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
-            "weight_GBps": round(wb / (avg / 1e3) / 1e9, 1), "alg_GBps": round(alg / (avg / 1e3) / 1e9, 1),
-            "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
-        }
+    per_shape = per_shape_stats(awq, lib, torch, hip, wl, layers, M, args.kernel_reps)
     # Context for the roofline: the achievable streaming-read rate at each
     # layer's size, and the same shapes as dense fp16 weights (W16A16).
     sr = stream_read_times(lib, torch, hip, layers, args.kernel_reps)
@@ -531,7 +606,6 @@ def main():
     eprint(f"[bench] per-kernel: " + ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s"
                                                for k, v in per_shape.items()))
 
-    del graph
     layers = None
     torch.cuda.empty_cache()
     fp16 = fp16_dense_times(torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], M, dev)
@@ -545,6 +619,34 @@ def main():
                 "layer_us": round(fp16_layer_ms * 1e3, 2), "w4a16_layer_us": round(w4_layer_ms * 1e3, 2),
                 "speedup_w4a16_over_fp16": round(fp16_layer_ms / w4_layer_ms, 3)}
     eprint(f"[bench] fp16 dense layer {fp16_layer_ms * 1e3:.1f} us vs W4A16 {w4_layer_ms * 1e3:.1f} us")
+
+    # Group size 64 (the Falcon-7B setting): the Falcon-7B-shaped decode stack.
+    g64 = None
+    if not args.no_g64:
+        wg = synth.FALCON_7B_DECODE_G64
+        eprint(f"[bench] building {wg.name}: {wg.layers} layers x {len(wg.shapes)} shapes, M={M}, G={wg.G}")
+        glayers, _ = build_stack(awq, torch, wg, M, dev, args.seed + 2)
+        gbytes = sum(weight_set_bytes(L.K, L.N, L.G) for _, L in glayers)
+        gwall, gev = time_stack_graph(lib, torch, glayers, args.steps, args.warmup)
+        gps = per_shape_stats(awq, lib, torch, hip, wg, glayers, M, args.kernel_reps)
+        g64 = {"workload": wg.name, "group": wg.G, "layers": wg.layers, "M": M,
+               "weight_bytes_per_step": gbytes, "ms_per_step": round(gwall, 5),
+               "value": round(gbytes / (gwall / 1e3) / 1e9, 1), "unit": "GB/s",
+               "pct_hbm_peak": round(100 * gbytes / (gwall / 1e3) / 1e9 / HBM_PEAK_GBS, 2), "per_kernel": gps}
+        eprint(f"[bench] G=64 stack: {gwall:.4f} ms/step, {g64['value']} GB/s; " +
+               ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s" for k, v in gps.items()))
+        glayers = None
+        torch.cuda.empty_cache()
+
+    # Gated epilogue (silu(gate) * up) on the fused gate+up layer.
+    gated = {"what": "awq_linear_silu_mul (silu(gate) * up in the kernel's epilogue) against awq_linear "
+                     "followed by torch silu and multiply on the halves",
+             "decode_llama2_7b_gate_up_M1": gated_times(awq, lib, torch, hip, 4096, 22016, 128, 1, dev, 24, 4)}
+    if not args.no_prefill:
+        gated["prefill_llama2_13b_gate_up_M2048"] = gated_times(awq, lib, torch, hip, 5120, 27648, 128, 2048, dev,
+                                                                  2, 10)
+    eprint("[bench] gated: " + ", ".join(f"{k}: fused {v['fused_us']}us vs unfused {v['unfused_us']}us"
+                                          for k, v in gated.items() if isinstance(v, dict)))
 
     qt = quantize_times(awq, torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], wl.G, dev)
     qdom = max(qt, key=lambda k: qt[k]["median_us"])
@@ -639,6 +741,8 @@ def main():
         "per_kernel": per_shape,
         "roofline": roofline,
         "fp16_dense_reference": fp16_ref,
+        "decode_g64": g64,
+        "gated": gated,
         "quantize": quantize,
         "prefill": prefill,
         "cpu_baseline": cpu,

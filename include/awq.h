@@ -196,6 +196,33 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
                      const awq_plan* plan, void* stream, void* start_event, void* stop_event);
 
 /*
+ * Gated MLP projection: the fused gate+up layer of a LLaMA-style MLP with its
+ * activation applied on the fp32 sums. W [K, N] holds the gate projection in
+ * columns 0 .. N/2-1 and the up projection in columns N/2 .. N-1 (the column
+ * order of a fused gate+up weight is not printed on the pages; this is the
+ * reading taken), and
+ *     y[m, i] = fp16( silu(g) * u ),  g = (x . W)[m, i],  u = (x . W)[m, N/2 + i],
+ *     silu(g) = g / (1 + exp(-g)),
+ * y is [M, N/2], 8-byte aligned. N % 32 == 0. TinyChat ("Speed Benchmarks",
+ * LLaMA-family models) fuses the small operators around its W4A16 kernels;
+ * here the activation runs in the decode kernel's epilogue (one launch, no
+ * [M, N] intermediate), or, on the prefill path, where the fp32 partial sums
+ * are added (the workspace then holds split_k * M * N fp32 values even for
+ * split_k = 1). Plans, workspace and errors as for awq_linear; the decode
+ * path needs M <= 16 and the LDS-staged variant with paired tiles.
+ */
+int awq_linear_silu_mul(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                        const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                        uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+int awq_linear_silu_mul_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                           uint16_t* y, void* workspace, size_t workspace_bytes,
+                           const awq_plan* plan, void* stream, void* start_event, void* stop_event);
+int awq_linear_silu_mul_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
+int awq_linear_silu_mul_workspace_bytes(int64_t M, int64_t K, int64_t N, int group,
+                                        const awq_plan* plan, size_t* bytes);
+
+/*
  * Measurement aid, not part of the layer: a plain streaming read of `bytes`
  * bytes (a multiple of 16) at device address `buf` (16-byte aligned) with
  * 16-byte loads, the achievable HBM read rate at that size against which a

@@ -112,8 +112,18 @@ FALCON_180B_STACK = Workload(
      Shape("up", 14848, 59392), Shape("down", 59392, 14848)),
     (1, 16), layers=80)
 
+# Falcon-7B-shaped decode stack at group size 64 (the group the TinyChat
+# README prescribes for Falcon-7B): 71 query heads + 1 shared key/value head
+# of dim 64 (hidden 4544), 4x MLP, 32 layers. K = 4544 is not a multiple of
+# 128, so the last 128-row band of every layer is ragged.
+FALCON_7B_DECODE_G64 = Workload(
+    "falcon-7b-decode-stack-g64",
+    (Shape("qkv", 4544, 4672), Shape("o", 4544, 4544),
+     Shape("up", 4544, 18176), Shape("down", 18176, 4544)),
+    (1, 8), G=64, layers=32)
+
 WORKLOADS = (SINGLE_4096, LLAMA2_7B_DECODE, LLAMA3_8B_SWEEP, LLAMA2_13B_PREFILL,
-             FALCON_180B_STACK)
+             FALCON_180B_STACK, FALCON_7B_DECODE_G64)
 
 
 def dense_weights(K: int, N: int, seed: int = 0, layer_id: int = 0, std: float = 0.02):

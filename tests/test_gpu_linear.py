@@ -31,6 +31,8 @@ SHAPES = [
     # (M, K, N, G)
     (1, 128, 16, 128), (1, 4096, 4096, 128), (3, 384, 40, 64), (16, 256, 24, 32), (5, 96, 8, 32),
     (17, 512, 136, 128), (33, 1024, 64, 64), (64, 640, 48, 128), (8, 11008, 128, 128), (2, 1024, 4104, 256),
+    # ragged last band (K not a multiple of 128)
+    (1, 4544, 72, 64), (4, 160, 24, 32), (9, 1216, 56, 64), (1, 32, 8, 32), (20, 1184, 40, 32),
 ]
 
 

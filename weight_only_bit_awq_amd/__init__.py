@@ -70,6 +70,19 @@ _SIGS = {
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_linear_silu_mul": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                           ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "awq_linear_silu_mul_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                              ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                              ctypes.POINTER(Plan), ctypes.c_void_p, ctypes.c_void_p,
+                                              ctypes.c_void_p]),
+    "awq_linear_silu_mul_plan": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                ctypes.POINTER(Plan)]),
+    "awq_linear_silu_mul_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                                           ctypes.c_int, ctypes.POINTER(Plan),
+                                                           ctypes.POINTER(ctypes.c_size_t)]),
     "awq_quantize": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "awq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
@@ -277,6 +290,53 @@ def linear(x, qweight, scales, zeros, N: int, group: int = 128, out=None, worksp
     return out
 
 
-__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_plan",
+def linear_silu_mul_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
+    p = _plan(plan) or Plan()
+    _check(library().awq_linear_silu_mul_plan(M, K, N, group, ctypes.byref(p)))
+    return {"path": p.path, "split_k": p.split_k, "waves": p.waves, "tpw": p.tpw, "x_stage": p.x_stage,
+            "tile": p.tile}
+
+
+def linear_silu_mul_workspace_bytes(M: int, K: int, N: int, group: int = 128, plan=None) -> int:
+    out = ctypes.c_size_t()
+    p = _plan(plan)
+    _check(library().awq_linear_silu_mul_workspace_bytes(M, K, N, group, ctypes.byref(p) if p else None,
+                                                         ctypes.byref(out)))
+    return int(out.value)
+
+
+def linear_silu_mul(x, qweight, scales, zeros, N: int, group: int = 128, out=None, workspace=None, plan=None):
+    """y[M, N/2] fp16 = silu(g) * u with [g | u] = x . W (W's first N/2
+    columns are the gate projection, the last N/2 the up projection)."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(qweight, torch.int32, "qweight")
+    _need(scales, torch.float16, "scales", 2)
+    _need(zeros, torch.int32, "zeros", 2)
+    M, K = x.shape
+    if scales.shape != (K // group, N) or zeros.shape != (K // group, N // 8):
+        raise ValueError("scales must be [K/G, N] and zeros [K/G, N/8]")
+    if qweight.numel() < qweight_words(K, N):
+        raise ValueError("qweight is smaller than the device layout needs")
+    if out is None:
+        out = torch.empty((M, N // 2), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out", 2)
+    p = _plan(plan)
+    nbytes = linear_silu_mul_workspace_bytes(M, K, N, group, p)
+    ws_ptr, ws_len = None, 0
+    if nbytes:
+        if workspace is None:
+            workspace = Workspace(x.device)
+        buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        ws_ptr, ws_len = buf.data_ptr(), buf.numel() * buf.element_size()
+    _check(library().awq_linear_silu_mul_ex(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                            M, K, N, group, out.data_ptr(), ws_ptr, ws_len,
+                                            ctypes.byref(p) if p else None, _stream(x.device), None, None))
+    return out
+
+
+__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_silu_mul",
+           "linear_silu_mul_plan", "linear_silu_mul_workspace_bytes", "linear_plan",
            "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",
            "abi_version"]

@@ -46,14 +46,27 @@ struct Resolved {
 
 constexpr int kDecodeMaxM = 64;
 
-int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out) {
+// Gated (silu(gate) * up) plans: on the decode path only the LDS-staged
+// variant with the gate and up tiles paired in one workgroup exists (half of
+// its waves on each tile), so the automatic choice takes the prefill path
+// whenever that does not fit.
+bool gated_decode_fits(int64_t M, int64_t K, int G, const awq_plan& p) {
+  if (M < 1 || M > 16 || p.tpw > 1 || p.x_stage == 2 || p.waves == 1) return false;
+  for (int w : {8, 4, 16})
+    if ((!p.waves || p.waves == w) && awq::decode_staged_fits((int)M, (int)K, G, w, 1)) return true;
+  return false;
+}
+
+int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out, bool gated = false) {
   awq_plan p = {};
   if (in) p = *in;
   if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2 ||
       p.tile < 0 || p.tile > 3)
     return AWQ_ERR_PLAN;
-  if (p.path == 0) p.path = (M <= kDecodeMaxM) ? 1 : 2;
+  if (gated && N % 32) return AWQ_ERR_SHAPE;
+  if (p.path == 0) p.path = gated ? (gated_decode_fits(M, K, G, p) ? 1 : 2) : (M <= kDecodeMaxM) ? 1 : 2;
   if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
+  if (p.path == 1 && gated && !gated_decode_fits(M, K, G, p)) return AWQ_ERR_PLAN;
   const int64_t KT = (K + 127) / 128;
   const int64_t NT = (N + 15) / 16;
   out->path = p.path;
@@ -78,6 +91,9 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     // layer has fewer than 8 full 128-row bands.
     int waves = p.waves;
     if (!waves) waves = (NT * 8 > 12288 || KT < 8) ? 4 : 8;
+    // gated: the same waves per workgroup, half on the gate tile and half on
+    // the up tile (measured on the LLaMA-2-7B gate+up layer at M = 1: as
+    // fast as the plain layer's eight waves on one tile; sixteen are slower)
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
@@ -105,8 +121,74 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     const int steps = awq::prefill_steps((int)K, out->tile);
     if (split > steps) split = steps > 0 ? steps : 1;
     out->split = split;
-    out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, split);
+    out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, split, gated);
   }
+  return AWQ_OK;
+}
+
+}  // namespace
+
+namespace {
+
+int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
+               int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+               const awq_plan* plan, void* stream, void* start_event, void* stop_event, bool gated) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, group, plan, &r, gated))) return st;
+  if (M == 0 || N == 0) return AWQ_OK;
+  if (!y) return AWQ_ERR_NULL;
+  const int64_t n_out = gated ? N / 2 : N;
+  if (K == 0) {
+    // Empty contraction: y = 0 (silu(0) * 0 = 0 for the gated form).
+    if (!aligned(y, 2)) return AWQ_ERR_ALIGN;
+    return hip_status(awq::launch_fill_zero(y, M * n_out, (hipStream_t)stream));
+  }
+  if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
+      !aligned(y, gated && r.path == 2 ? 8 : 2))
+    return AWQ_ERR_ALIGN;
+  if (r.ws_bytes) {
+    if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return AWQ_ERR_ALIGN;
+  }
+  if (M * K * 2 >= ((int64_t)1 << 31) || (K / group) * N * 2 >= ((int64_t)1 << 31))
+    return AWQ_ERR_SHAPE;  // the kernels address x and scales with 32-bit buffer offsets
+  awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
+  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  if (r.path == 1) {
+    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1, gated};
+    return hip_status(awq::launch_decode(a, cfg, L));
+  }
+  return hip_status(awq::launch_prefill(a, r.tile, r.split, static_cast<float*>(workspace), gated, L));
+}
+
+int plan_out(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan, bool gated) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (!plan) return AWQ_ERR_NULL;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, group, plan, &r, gated))) return st;
+  plan->path = r.path;
+  plan->split_k = r.split;
+  plan->waves = r.waves;
+  plan->tpw = r.tpw;
+  plan->x_stage = r.x_stage;
+  plan->tile = r.tile;
+  return AWQ_OK;
+}
+
+int workspace_out(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan, size_t* bytes, bool gated) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if ((st = check_layer(K, N, group))) return st;
+  if (!bytes) return AWQ_ERR_NULL;
+  Resolved r;
+  if ((st = resolve_plan(M, K, N, group, plan, &r, gated))) return st;
+  *bytes = (M == 0 || K == 0 || N == 0) ? 0 : r.ws_bytes;
   return AWQ_OK;
 }
 
@@ -190,31 +272,12 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
 }
 
 int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) {
-  int st = check_dims(M, K, N);
-  if (st) return st;
-  if ((st = check_layer(K, N, group))) return st;
-  if (!plan) return AWQ_ERR_NULL;
-  Resolved r;
-  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
-  plan->path = r.path;
-  plan->split_k = r.split;
-  plan->waves = r.waves;
-  plan->tpw = r.tpw;
-  plan->x_stage = r.x_stage;
-  plan->tile = r.tile;
-  return AWQ_OK;
+  return plan_out(M, K, N, group, plan, false);
 }
 
 int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
                                   size_t* bytes) {
-  int st = check_dims(M, K, N);
-  if (st) return st;
-  if ((st = check_layer(K, N, group))) return st;
-  if (!bytes) return AWQ_ERR_NULL;
-  Resolved r;
-  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
-  *bytes = (M == 0 || K == 0 || N == 0) ? 0 : r.ws_bytes;
-  return AWQ_OK;
+  return workspace_out(M, K, N, group, plan, bytes, false);
 }
 
 int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes) {
@@ -224,34 +287,32 @@ int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_
 int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                      int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
                      const awq_plan* plan, void* stream, void* start_event, void* stop_event) {
-  int st = check_dims(M, K, N);
-  if (st) return st;
-  if ((st = check_layer(K, N, group))) return st;
-  Resolved r;
-  if ((st = resolve_plan(M, K, N, group, plan, &r))) return st;
-  if (M == 0 || N == 0) return AWQ_OK;
-  if (!y) return AWQ_ERR_NULL;
-  if (K == 0) {
-    // Empty contraction: y = 0.
-    if (!aligned(y, 2)) return AWQ_ERR_ALIGN;
-    return hip_status(awq::launch_fill_zero(y, M * N, (hipStream_t)stream));
-  }
-  if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) || !aligned(y, 2))
-    return AWQ_ERR_ALIGN;
-  if (r.ws_bytes) {
-    if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
-    if (!aligned(workspace, 16)) return AWQ_ERR_ALIGN;
-  }
-  if (M * K * 2 >= ((int64_t)1 << 31) || (K / group) * N * 2 >= ((int64_t)1 << 31))
-    return AWQ_ERR_SHAPE;  // the kernels address x and scales with 32-bit buffer offsets
-  awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
-  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
-  if (r.path == 1) {
-    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1};
-    return hip_status(awq::launch_decode(a, cfg, L));
-  }
-  return hip_status(awq::launch_prefill(a, r.tile, r.split, static_cast<float*>(workspace), L));
+  return run_linear(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, plan, stream,
+                    start_event, stop_event, false);
+}
+
+int awq_linear_silu_mul_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                           const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group, uint16_t* y,
+                           void* workspace, size_t workspace_bytes, const awq_plan* plan, void* stream,
+                           void* start_event, void* stop_event) {
+  return run_linear(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, plan, stream,
+                    start_event, stop_event, true);
+}
+
+int awq_linear_silu_mul(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                        int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  return run_linear(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream,
+                    nullptr, nullptr, true);
+}
+
+int awq_linear_silu_mul_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) {
+  return plan_out(M, K, N, group, plan, true);
+}
+
+int awq_linear_silu_mul_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
+                                        size_t* bytes) {
+  return workspace_out(M, K, N, group, plan, bytes, true);
 }
 
 int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,

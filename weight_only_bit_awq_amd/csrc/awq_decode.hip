@@ -35,8 +35,10 @@
 //   * Rows >= M and columns >= N read as zero (out-of-range buffer offsets) or
 //     are never stored, so loops have no data-dependent branches; past a
 //     wave's last tile the prefetch index is clamped and the result is scaled
-//     by zero. A ragged last band (K not a multiple of 128) is handled after
-//     the loop with explicit masks.
+//     by zero. A ragged last band (K not a multiple of 128) runs through the
+//     loop like the others: its activations past K are zero (zero padding of
+//     the staged rows; out-of-range loads in the streamed variant), and its
+//     padding rows hold code 0 with the last group's (finite) scale.
 //   * The waves' fp32 results are summed through LDS in a fixed order and
 //     stored as fp16. Workgroup ids are remapped so neighbouring tiles run on
 //     the same XCD.
@@ -71,7 +73,7 @@ __device__ __forceinline__ float scale_of(uint32_t bits) {
 // ---------------------------------------------------------------------------
 
 struct StagedLayout {
-  uint32_t x_row;        // bytes per staged activation row (K padded to >= 128, + 16)
+  uint32_t x_row;        // bytes per staged activation row (K zero-padded to whole bands, + 16)
   uint32_t x_chunks;     // 16-byte chunks per staged row
   uint32_t scratch_off;  // per-thread 16-byte slots for masked staging stores
 };
@@ -85,25 +87,33 @@ struct BandBuf {
   uint32_t zw[TPW][NG];
 };
 
-template <int TPW, int GPT, int WAVES, int DEPTH, int S>
-__global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_t* __restrict__ x,
-                                                                   const u4* __restrict__ qw,
-                                                                   const uint16_t* __restrict__ scales,
-                                                                   const uint32_t* __restrict__ zeros,
-                                                                   uint16_t* __restrict__ y, int M, int K, int N,
-                                                                   int G, int NT, StagedLayout lay) {
+// TM: 1 = one 16-column tile per workgroup, 2 = two adjacent tiles, 3 = the
+// gated epilogue: tile t of the first half of the columns (gate) and tile t
+// of the second half (up) in one workgroup, the first WAVES/2 waves on the
+// gate tile and the others on the up tile (each wave holds one tile, so the
+// register footprint is that of TM = 1), stored as y[m, n] = silu(gate) * up.
+template <int TM, int GPT, int WAVES, int DEPTH, int S>
+__device__ __forceinline__ void decode_staged_body(const uint16_t* __restrict__ x, const u4* __restrict__ qw,
+                                                   const uint16_t* __restrict__ scales,
+                                                   const uint32_t* __restrict__ zeros, uint16_t* __restrict__ y,
+                                                   int M, int K, int N, int G, int NT, StagedLayout lay) {
   using GB = GroupsPerBand<GPT>;
+  constexpr int TPW = TM == 2 ? 2 : 1;
+  constexpr bool GATED = TM == 3;
+  static_assert(!GATED || WAVES % 2 == 0, "gated: an even number of waves");
+  constexpr int WK = GATED ? WAVES / 2 : WAVES;  // waves that split one tile's K range
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int NTH = 64 * WAVES;
   const int wg = xcd_remap(blockIdx.x, gridDim.x);
-  const int t0 = wg * TPW;
   const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // gated: waves WK.. take the up tile, NT/2 tiles after the gate tile
+  const int w = GATED ? wid % WK : wid;
+  const int t0 = GATED ? wg + (wid >= WK ? NT / 2 : 0) : wg * TPW;
   const int h = lane >> 4;
   const int groups = K / G;
   const int tpg = G / 128;
   const int KT = (K + 127) / 128;
-  const int KTF = K / 128;
 
   const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   const rsrc_t rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
@@ -129,14 +139,15 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   //    Offsets are below 2^31, so setting bit 31 makes a masked load read
   //    zero; group indices are clamped to the last group (a ragged band's
   //    missing groups are then never used with nonzero weight).
-  const int n_my = KTF > w ? (KTF - w + WAVES - 1) / WAVES : 0;
-  const int last = max(w + WAVES * (n_my - 1), 0);
+  const int n_my = KT > w ? (KT - w + WK - 1) / WK : 0;
+  const int last = max(w + WK * (n_my - 1), 0);
   const u4* qcol[TPW];
   uint32_t soff[TPW], zoff[TPW];
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt) {
-    qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
-    const uint32_t col = 16u * (t0 + tt) + (lane & 15u);
+    const int ti = t0 + tt;
+    qcol[tt] = qw + (int64_t)min(ti, NT - 1) * 64 + lane;
+    const uint32_t col = 16u * ti + (lane & 15u);
     const uint32_t bad = (uint32_t)!(col < (uint32_t)N) << 31;
     soff[tt] = (col * 2u) | bad;
     zoff[tt] = ((col >> 3) * 4u) | bad;
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   };
   BandBuf<TPW, GB::NG> buf[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_band(buf[d], min(w + WAVES * d, last));
+  for (int d = 0; d < DEPTH; ++d) load_band(buf[d], min(w + WK * d, last));
 
   // 3. Staging stores (masked ones go to this thread's scratch slot) and barrier.
 #pragma unroll
@@ -207,41 +218,17 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int i = r * DEPTH + d;
-      consume(buf[d], w + WAVES * i, 1.f);
-      load_band(buf[d], min(w + WAVES * (i + DEPTH), last));
+      consume(buf[d], w + WK * i, 1.f);
+      load_band(buf[d], min(w + WK * (i + DEPTH), last));
     }
   }
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     const int i = (rounds - 1) * DEPTH + d;
-    consume(buf[d], min(w + WAVES * i, last), i < n_my ? 1.f : 0.f);
+    consume(buf[d], min(w + WK * i, last), i < n_my ? 1.f : 0.f);
   }
 
-  // 5. Ragged last band: blocks past K are skipped; groups past the last one
-  //    hold no data and are skipped as well.
-  if (KTF < KT && w == (KTF % WAVES)) {
-    BandBuf<TPW, GB::NG> b;
-    load_band(b, KTF);
-    const int valid_blocks = (K - 128 * KTF) / 32;
-#pragma unroll
-    for (int tt = 0; tt < TPW; ++tt)
-#pragma unroll
-      for (int gi = 0; gi < GB::NG; ++gi) {
-        if (gi * GB::JPG >= valid_blocks) continue;
-        const ZeroConst zc = zero_const(zero_nibble(b.zw[tt][gi], lcol));
-        f4 accg = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int jj = 0; jj < GB::JPG; ++jj) {
-          const int j = gi * GB::JPG + jj;
-          if (j < valid_blocks)
-            accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8*>(xrow + 256 * KTF + 64 * j),
-                                                          decode_diff_vk(b.wq[tt][j], zc, kc), accg, 0, 0, 0);
-        }
-        acc[tt] += scale_of(b.s[tt][gi]) * accg;
-      }
-  }
-
-  // 6. Sum the waves' results through LDS (the staging area is reused) and
+  // 5. Sum the waves' results through LDS (the staging area is reused) and
   //    store. Lane l, register r of tile tt holds output row 4(l/16) + r,
   //    column 16(t0 + tt) + l%16.
   __syncthreads();
@@ -249,17 +236,52 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
 #pragma unroll
   for (int tt = 0; tt < TPW; ++tt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[((w * TPW + tt) * 4 + r) * 64 + lane] = acc[tt][r];
+    for (int r = 0; r < 4; ++r) red[((wid * TPW + tt) * 4 + r) * 64 + lane] = acc[tt][r];
   __syncthreads();
-  for (int o = threadIdx.x; o < TPW * 256; o += NTH) {
-    float v = 0.f;
+  if constexpr (GATED) {
+    // gate: waves 0 .. WK-1, up: waves WK .. WAVES-1, same (row, column) at the same offset
+    const int NO = N / 2;
+    for (int o = threadIdx.x; o < 256; o += NTH) {
+      float vg = 0.f, vu = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < WAVES; ++ww) v += red[ww * TPW * 256 + o];
-    const int ol = o & 63, r = (o >> 6) & 3, tt = o >> 8;
-    const int row = 4 * (ol >> 4) + r;
-    const int cc = 16 * (t0 + tt) + (ol & 15);
-    if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      for (int ww = 0; ww < WK; ++ww) vg += red[ww * 256 + o], vu += red[(WK + ww) * 256 + o];
+      const int ol = o & 63, r = o >> 6;
+      const int row = 4 * (ol >> 4) + r;
+      const int cc = 16 * wg + (ol & 15);
+      if (row < M && cc < NO) y[(int64_t)row * NO + cc] = __builtin_bit_cast(uint16_t, (_Float16)(vg / (1.f + expf(-vg)) * vu));
+    }
+  } else {
+    for (int o = threadIdx.x; o < TPW * 256; o += NTH) {
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < WAVES; ++ww) v += red[ww * TPW * 256 + o];
+      const int ol = o & 63, r = (o >> 6) & 3, tt = o >> 8;
+      const int row = 4 * (ol >> 4) + r;
+      const int cc = 16 * (t0 + tt) + (ol & 15);
+      if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+    }
   }
+}
+
+template <int TM, int GPT, int WAVES, int DEPTH, int S>
+__global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_t* __restrict__ x,
+                                                                   const u4* __restrict__ qw,
+                                                                   const uint16_t* __restrict__ scales,
+                                                                   const uint32_t* __restrict__ zeros,
+                                                                   uint16_t* __restrict__ y, int M, int K, int N,
+                                                                   int G, int NT, StagedLayout lay) {
+  decode_staged_body<TM, GPT, WAVES, DEPTH, S>(x, qw, scales, zeros, y, M, K, N, G, NT, lay);
+}
+
+// The same kernel held to 64 VGPRs, i.e. eight waves per SIMD: used where
+// that costs no spills (one tile per wave, one group per band), so that four
+// 8-wave (or two 16-wave) workgroups fit on a CU.
+template <int TM, int GPT, int WAVES, int DEPTH, int S>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(8))) void decode_staged_kernel_o8(
+    const uint16_t* __restrict__ x, const u4* __restrict__ qw, const uint16_t* __restrict__ scales,
+    const uint32_t* __restrict__ zeros, uint16_t* __restrict__ y, int M, int K, int N, int G, int NT,
+    StagedLayout lay) {
+  decode_staged_body<TM, GPT, WAVES, DEPTH, S>(x, qw, scales, zeros, y, M, K, N, G, NT, lay);
 }
 
 // ---------------------------------------------------------------------------
@@ -282,6 +304,7 @@ struct StreamCtx {
   uint32_t soff, zoff;  // byte offsets of this lane's scale / zero word, or kOOB
   uint32_t srow, zrow;  // bytes per group row of scales / zeros
   int tpg;
+  int K;
 };
 
 template <int MT, int GPT>
@@ -295,11 +318,15 @@ __device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const StreamCtx&
     b.zw[gi] = __builtin_amdgcn_raw_buffer_load_b32(c.rz, c.zoff + g * c.zrow, 0, 0);
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int j = 0; j < 4; ++j) {
+    // 32-row blocks past K (in a ragged last band) read zero activations
+    const bool blk = 128 * kt + 32 * j < c.K;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int mt = 0; mt < MT; ++mt)
       b.xa[mt][j] = __builtin_bit_cast(
-          u4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, c.xoff[mt] + 256u * (uint32_t)kt + 64u * j, 0, 0));
+          u4, __builtin_amdgcn_raw_buffer_load_b128(c.rx, blk ? c.xoff[mt] + 256u * (uint32_t)kt + 64u * j : kOOB,
+                                                    0, 0));
+  }
 }
 
 template <int MT, int GPT>
@@ -356,10 +383,10 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
   c.srow = (uint32_t)N * 2u;
   c.zrow = (uint32_t)(N / 8) * 4u;
   c.tpg = G / 128;
+  c.K = K;
   const DecodeConsts kc = decode_consts();
 
-  const int KTF = K / 128;
-  const int n_my = KTF > w ? (KTF - w + WAVES - 1) / WAVES : 0;
+  const int n_my = KT > w ? (KT - w + WAVES - 1) / WAVES : 0;
   const int last = max(w + WAVES * (n_my - 1), 0);
 
   f4 acc[MT];
@@ -382,21 +409,6 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
   for (int d = 0; d < DEPTH; ++d) {
     const int i = (rounds - 1) * DEPTH + d;
     consume_bundle<MT, GPT>(buf[d], acc, col, i < n_my ? 1.f : 0.f, kc);
-  }
-
-  // Ragged last band: its activation loads are masked per 32-row block;
-  // padding blocks also read zero scales and zero points (their group index is
-  // out of range), so they add nothing.
-  if (KTF < KT && w == (KTF % WAVES)) {
-    Bundle<MT, GPT> b;
-    load_bundle<MT, GPT>(b, c, KTF);
-    const int valid_blocks = (K - 128 * KTF) / 32;
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j >= valid_blocks) b.xa[mt][j] = u4{0u, 0u, 0u, 0u};
-    consume_bundle<MT, GPT>(b, acc, col, 1.f, kc);
   }
 
   // Sum the waves' partial tiles. Lane l, register r of 16-row tile mt holds
@@ -447,8 +459,9 @@ struct StagedSizes {
 StagedSizes staged_sizes(int M, int K, int G, int waves, int tpw) {
   StagedSizes z;
   const int nth = 64 * waves;
-  const uint32_t kp = (uint32_t)(K < 128 ? 128 : K);
-  z.lay.x_chunks = kp / 8 + 1;  // one extra 16-byte chunk of padding per row
+  // rows padded with zeros to whole 128-row bands, plus one 16-byte chunk
+  const uint32_t kp = (uint32_t)((K + 127) / 128 * 128);
+  z.lay.x_chunks = kp / 8 + 1;
   z.lay.x_row = z.lay.x_chunks * 16;
   z.lay.scratch_off = (uint32_t)M * z.lay.x_row;
   const size_t lds = z.lay.scratch_off + (size_t)nth * 16;
@@ -467,45 +480,52 @@ hipError_t allow_lds(F kernel, size_t lds) {
                              (int)lds);
 }
 
-template <int TPW, int GPT, int WAVES, int S>
-hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
+template <int TM, int WAVES, typename F>
+hipError_t launch_staged_k(F k, const LinearArgs& a, const StagedSizes& z, const Launch& L) {
   const int NT = (a.N + 15) / 16;
-  auto k = decode_staged_kernel<TPW, GPT, WAVES, kStagedDepth, S>;
   hipError_t e = allow_lds(k, z.lds);
   if (e != hipSuccess) return e;
-  const unsigned grid = (unsigned)((NT + TPW - 1) / TPW);
+  const unsigned grid = (unsigned)(TM == 1 ? NT : TM == 2 ? (NT + 1) / 2 : NT / 2);
   return launch_kernel(k, dim3(grid), dim3(64 * WAVES), z.lds, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales,
                        a.zeros, a.y, a.M, a.K, a.N, a.G, NT, z.lay);
 }
 
-template <int TPW, int GPT, int WAVES>
+template <int TM, int GPT, int WAVES, int S>
+hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
+  if constexpr (TM != 2 && GPT == 1)
+    return launch_staged_k<TM, WAVES>(decode_staged_kernel_o8<TM, GPT, WAVES, kStagedDepth, S>, a, z, L);
+  else
+    return launch_staged_k<TM, WAVES>(decode_staged_kernel<TM, GPT, WAVES, kStagedDepth, S>, a, z, L);
+}
+
+template <int TM, int GPT, int WAVES>
 hipError_t launch_staged_w(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
   switch (z.S) {
-    case 1: return launch_staged_s<TPW, GPT, WAVES, 1>(a, z, L);
-    case 2: return launch_staged_s<TPW, GPT, WAVES, 2>(a, z, L);
-    case 4: return launch_staged_s<TPW, GPT, WAVES, 4>(a, z, L);
-    case 8: return launch_staged_s<TPW, GPT, WAVES, 8>(a, z, L);
+    case 1: return launch_staged_s<TM, GPT, WAVES, 1>(a, z, L);
+    case 2: return launch_staged_s<TM, GPT, WAVES, 2>(a, z, L);
+    case 4: return launch_staged_s<TM, GPT, WAVES, 4>(a, z, L);
+    case 8: return launch_staged_s<TM, GPT, WAVES, 8>(a, z, L);
   }
   return hipErrorInvalidValue;
 }
 
-template <int TPW, int GPT>
+template <int TM, int GPT>
 hipError_t launch_staged_g(const LinearArgs& a, int waves, const StagedSizes& z, const Launch& L) {
   switch (waves) {
-    case 2: return launch_staged_w<TPW, GPT, 2>(a, z, L);
-    case 4: return launch_staged_w<TPW, GPT, 4>(a, z, L);
-    case 8: return launch_staged_w<TPW, GPT, 8>(a, z, L);
-    case 16: return launch_staged_w<TPW, GPT, 16>(a, z, L);
+    case 2: return launch_staged_w<TM, GPT, 2>(a, z, L);
+    case 4: return launch_staged_w<TM, GPT, 4>(a, z, L);
+    case 8: return launch_staged_w<TM, GPT, 8>(a, z, L);
+    case 16: return launch_staged_w<TM, GPT, 16>(a, z, L);
   }
   return hipErrorInvalidValue;
 }
 
-template <int TPW>
+template <int TM>
 hipError_t launch_staged_t(const LinearArgs& a, int waves, const StagedSizes& z, const Launch& L) {
-  if (a.G == 32) return launch_staged_g<TPW, 4>(a, waves, z, L);
-  if (a.G == 64) return launch_staged_g<TPW, 2>(a, waves, z, L);
-  if (a.G == 128) return launch_staged_g<TPW, 1>(a, waves, z, L);
-  return launch_staged_g<TPW, 0>(a, waves, z, L);
+  if (a.G == 32) return launch_staged_g<TM, 4>(a, waves, z, L);
+  if (a.G == 64) return launch_staged_g<TM, 2>(a, waves, z, L);
+  if (a.G == 128) return launch_staged_g<TM, 1>(a, waves, z, L);
+  return launch_staged_g<TM, 0>(a, waves, z, L);
 }
 
 template <int MT, int GPT, int WAVES>
@@ -545,6 +565,12 @@ bool decode_staged_fits(int M, int K, int G, int waves, int tpw) {
 }
 
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L) {
+  if (cfg.gated) {
+    // gate and up halves paired in one workgroup: needs the staged variant
+    if (!cfg.staged || a.N % 32 || cfg.waves < 2 || !decode_staged_fits(a.M, a.K, a.G, cfg.waves, 1))
+      return hipErrorInvalidValue;
+    return launch_staged_t<3>(a, cfg.waves, staged_sizes(a.M, a.K, a.G, cfg.waves, 1), L);
+  }
   if (cfg.staged) {
     if (!decode_staged_fits(a.M, a.K, a.G, cfg.waves, cfg.tpw)) return hipErrorInvalidValue;
     const StagedSizes z = staged_sizes(a.M, a.K, a.G, cfg.waves, cfg.tpw);

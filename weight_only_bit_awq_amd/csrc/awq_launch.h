@@ -56,6 +56,7 @@ struct DecodeConfig {
   int waves;
   int tpw;
   bool staged;
+  bool gated;  // y[M, N/2] = silu(x W[:, :N/2]) * (x W[:, N/2:]); staged only, N % 32 == 0
 };
 bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L);
@@ -68,9 +69,11 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
 int prefill_steps(int K, int tile);
 // Fills *tile and/or *splits where they are 0, from a cost model.
 void prefill_auto_plan(int M, int K, int N, int* tile, int* splits);
-size_t prefill_workspace_bytes(int M, int N, int splits);
+// Gated (y[M, N/2] = silu(gate) * up): the partials always go through the
+// workspace and the reduction applies the epilogue.
+size_t prefill_workspace_bytes(int M, int N, int splits, bool gated);
 bool prefill_fits(int K, int N);
-hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, const Launch& L);
+hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
 // Plain streaming read of `bytes` (a multiple of 16) at `buf`; the 16 bytes at
 // `sink` may receive a value derived from the data.

@@ -95,7 +95,13 @@ __device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
   return row * (16u * CPR) + ((chunk ^ (row % CPR)) << 4);
 }
 
-template <int WM, int WN, int MTW, int NTW, int KS, int GS>
+// EPI = true: gated epilogue. The workgroup's BN logical columns are BN/2
+// gate columns g0 .. g0+BN/2-1 followed by the matching up columns N/2 + g0 ..;
+// each wave holds NTW/2 gate tiles and the NTW/2 up tiles of the same
+// columns, so silu(gate) * up is formed in registers and y is [M, N/2]
+// (with split-K the fp32 partials go to the workspace at their global
+// columns and the reduction applies the epilogue).
+template <int WM, int WN, int MTW, int NTW, int KS, int GS, bool EPI>
 __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* __restrict__ x,
                                                                const uint32_t* __restrict__ qw,
                                                                const uint16_t* __restrict__ scales,
@@ -114,7 +120,12 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   const int mtile = tile % n_mtiles;
   const int ntile = tile / n_mtiles;
   const int m0 = mtile * C::BM;
-  const int n0 = ntile * C::BN;
+  const int n0 = ntile * C::BN;  // plain: first global column of the workgroup
+  const int NO = N / 2;           // gated: columns per half
+  const int g0 = ntile * (C::BN / 2);  // gated: first gate column of the workgroup
+  // logical column c of the workgroup tile -> global column, and whether it exists
+  auto gcol = [&](int c) { return EPI ? (c < C::BN / 2 ? g0 + c : NO + g0 + (c - C::BN / 2)) : n0 + c; };
+  auto gvalid = [&](int c) { return EPI ? g0 + (c % (C::BN / 2)) < NO : n0 + c < N; };
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -144,16 +155,22 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   }
   // Dword tid of the scale region: columns 2c, 2c+1 of group row gi; of the
   // zero region: packed word c of group row gi.
-  const int sc_gi = tid / (C::BN / 2), sc_col = n0 + 2 * (tid % (C::BN / 2));
-  const bool sc_ok = sc_gi < GS && sc_col < N;
-  const int zw_gi = tid / (C::BN / 8), zw_w = n0 / 8 + tid % (C::BN / 8);
-  const bool zw_ok = zw_gi < GS && zw_w < N / 8;
+  const int sc_gi = tid / (C::BN / 2), sc_col = gcol(2 * (tid % (C::BN / 2)));
+  const bool sc_ok = sc_gi < GS && gvalid(2 * (tid % (C::BN / 2)));
+  const int zw_gi = tid / (C::BN / 8), zw_w = gcol(8 * (tid % (C::BN / 8))) / 8;
+  const bool zw_ok = zw_gi < GS && gvalid(8 * (tid % (C::BN / 8)));
+  // Logical column (within the workgroup tile) of the wave's column tile nt;
+  // gated: tiles 0 .. NTW/2-1 are gate columns, the rest the up columns of
+  // the same outputs.
+  auto lcol = [&](int nt) {
+    return EPI ? (nt < NTW / 2 ? 0 : C::BN / 2) + 16 * (NTW / 2) * wn + 16 * (nt % (NTW / 2)) : 16 * (NTW * wn + nt);
+  };
   // This lane's slice of each of the wave's NTW column tiles in band 0.
   uint32_t b_off[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    const int ct = n0 / 16 + NTW * wn + nt;
-    b_off[nt] = ct < NT ? (uint32_t)ct * 1024u + (uint32_t)lane * 16u : kOOB;
+    const int ct = gcol(lcol(nt)) / 16;
+    b_off[nt] = gvalid(lcol(nt)) ? (uint32_t)ct * 1024u + (uint32_t)lane * 16u : kOOB;
   }
 
   auto issue_stage = [&](int step, int buf) {
@@ -190,7 +207,6 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
 
   const DecodeConsts kc = decode_consts();
   const int arow0 = 16 * MTW * wm + (lane & 15);
-  const int ccol0 = 16 * NTW * wn + (lane & 15);  // column within the workgroup tile, nt = 0
   for (int step = step0; step < step1; ++step) {
     // Wait for this wave's loads of the current stage, then for everyone's;
     // the barrier also frees the other buffer (read during the last step).
@@ -215,7 +231,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
       if (s == 0 || (GS > 1 && s % (C::KB / GS) == 0)) {
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
-          const int c = ccol0 + 16 * nt;
+          const int c = lcol(nt) + (lane & 15);
           const uint32_t zw = zw_l[gi * (C::BN / 8) + c / 8];
           zc[nt] = zero_const((zw >> (4 * (c % 8))) & 0xFu);
           s2[nt] = splat_h2(sc_l[gi * C::BN + c]);
@@ -240,16 +256,33 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   }
 
   // Lane l, register r of tile (mt, nt): row 4(l/16) + r, column l%16.
+  if (EPI && !ws) {
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NTW / 2; ++nt) {
+        const int c = lcol(nt) + (lane & 15);
+        const int col = gcol(c);  // gate column = output column
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = m0 + 16 * (MTW * wm + mt) + 4 * h + r;
+          const float g = acc[mt][nt][r], v = acc[mt][nt + NTW / 2][r];
+          if (row < M && gvalid(c)) y[(int64_t)row * NO + col] = __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + expf(-g)) * v));
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      const int col = n0 + ccol0 + 16 * nt;
+      const int c = lcol(nt) + (lane & 15);
+      const int col = gcol(c);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = m0 + 16 * (MTW * wm + mt) + 4 * h + r;
         const float v = acc[mt][nt][r];
-        if (row < M && col < N) {
+        if (row < M && gvalid(c)) {
           if (ws)
             ws[((int64_t)split * M + row) * N + col] = v;
           else
@@ -273,20 +306,46 @@ __global__ __launch_bounds__(256) void prefill_reduce_kernel(const float* __rest
   *reinterpret_cast<us4*>(y + i) = o;
 }
 
+// Gated epilogue: y[m, i] = fp16(silu(g) * u) with g = sum over s of
+// ws[s][m][i] and u = sum over s of ws[s][m][N/2 + i] (increasing s); four
+// outputs per thread. N/2 is a multiple of 4.
+__global__ __launch_bounds__(256) void prefill_reduce_silu_mul_kernel(const float* __restrict__ ws,
+                                                                      uint16_t* __restrict__ y, int M, int N,
+                                                                      int splits) {
+  const int NO = N / 2;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= (int64_t)M * NO) return;
+  const int64_t m = i / NO, c = i % NO;
+  const int64_t mn = (int64_t)M * N;
+  const float* gp = ws + m * N + c;
+  f4 g = *reinterpret_cast<const f4*>(gp);
+  f4 u = *reinterpret_cast<const f4*>(gp + NO);
+  for (int s = 1; s < splits; ++s) {
+    g += *reinterpret_cast<const f4*>(gp + s * mn);
+    u += *reinterpret_cast<const f4*>(gp + s * mn + NO);
+  }
+  typedef uint16_t us4 __attribute__((ext_vector_type(4)));
+  us4 o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) o[e] = __builtin_bit_cast(uint16_t, (_Float16)(g[e] / (1.f + expf(-g[e])) * u[e]));
+  *reinterpret_cast<us4*>(y + i) = o;
+}
+
 namespace {
 
-template <int WM, int WN, int MTW, int NTW, int KS, int GS>
-hipError_t launch_prefill_t(const LinearArgs& a, int splits, float* ws, const Launch& L) {
+template <int WM, int WN, int MTW, int NTW, int KS, int GS, bool EPI>
+hipError_t launch_prefill_e(const LinearArgs& a, int splits, float* ws, const Launch& L) {
+  constexpr bool gated = EPI;
   using C = PrefillCfg<WM, WN, MTW, NTW, KS, GS>;
   const int NT = (a.N + 15) / 16;
   const int KT = (a.K + 127) / 128;
   const int n_mtiles = (a.M + C::BM - 1) / C::BM;
-  const int n_ntiles = (a.N + C::BN - 1) / C::BN;
+  const int n_ntiles = EPI ? (a.N / 2 + C::BN / 2 - 1) / (C::BN / 2) : (a.N + C::BN - 1) / C::BN;
   const int nsteps = (a.K + KS - 1) / KS;
   // Steps per split rounded so that every split is non-empty.
   const int split_steps = (nsteps + splits - 1) / splits;
   splits = (nsteps + split_steps - 1) / split_steps;
-  auto k = prefill_kernel<WM, WN, MTW, NTW, KS, GS>;
+  auto k = prefill_kernel<WM, WN, MTW, NTW, KS, GS, EPI>;
   if (C::LDS_BYTES > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        C::LDS_BYTES);
@@ -294,6 +353,8 @@ hipError_t launch_prefill_t(const LinearArgs& a, int splits, float* ws, const La
   }
   const uint32_t qw_bytes = (uint32_t)((size_t)NT * KT * 1024);
   const int n_tiles = n_mtiles * n_ntiles;
+  // fp32 partials go to the workspace when K is split (the gated epilogue is
+  // then applied where they are added)
   float* part = splits > 1 ? ws : nullptr;
   const Launch first{L.stream, L.start, part ? nullptr : L.stop};
   hipError_t e = launch_kernel(k, dim3((unsigned)(n_tiles * splits)), dim3(C::NTH), C::LDS_BYTES, first, a.x, a.qw,
@@ -302,19 +363,29 @@ hipError_t launch_prefill_t(const LinearArgs& a, int splits, float* ws, const La
   if (e != hipSuccess || !part) return e;
   const int64_t mn = (int64_t)a.M * a.N;
   const Launch second{L.stream, nullptr, L.stop};
+  if (gated)
+    return launch_kernel(prefill_reduce_silu_mul_kernel, dim3((unsigned)((mn / 2 / 4 + 255) / 256)), dim3(256), 0,
+                         second, static_cast<const float*>(part), a.y, a.M, a.N, splits);
   return launch_kernel(prefill_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, second, part, a.y,
                        mn, splits);
 }
 
+template <int WM, int WN, int MTW, int NTW, int KS, int GS>
+hipError_t launch_prefill_t(const LinearArgs& a, int splits, float* ws, bool gated, const Launch& L) {
+  if (gated) return launch_prefill_e<WM, WN, MTW, NTW, KS, GS, true>(a, splits, ws, L);
+  return launch_prefill_e<WM, WN, MTW, NTW, KS, GS, false>(a, splits, ws, L);
+}
+
 // Groups per step: KS / G for G < KS, else 1 (G is then a multiple of KS).
 template <int WM, int WN, int MTW, int NTW, int KS>
-hipError_t launch_prefill_k(const LinearArgs& a, int splits, float* ws, const Launch& L) {
+hipError_t launch_prefill_k(const LinearArgs& a, int splits, float* ws, bool gated, const Launch& L) {
   if (a.G < KS) {
-    if (KS / a.G == 2) return launch_prefill_t<WM, WN, MTW, NTW, KS, 2>(a, splits, ws, L);
-    if (KS == 128 && a.G == 32) return launch_prefill_t<WM, WN, MTW, NTW, KS, (KS == 128 ? 4 : 2)>(a, splits, ws, L);
+    if (KS / a.G == 2) return launch_prefill_t<WM, WN, MTW, NTW, KS, 2>(a, splits, ws, gated, L);
+    if (KS == 128 && a.G == 32)
+      return launch_prefill_t<WM, WN, MTW, NTW, KS, (KS == 128 ? 4 : 2)>(a, splits, ws, gated, L);
     return hipErrorInvalidValue;
   }
-  return launch_prefill_t<WM, WN, MTW, NTW, KS, 1>(a, splits, ws, L);
+  return launch_prefill_t<WM, WN, MTW, NTW, KS, 1>(a, splits, ws, gated, L);
 }
 
 }  // namespace
@@ -379,19 +450,21 @@ void prefill_auto_plan(int M, int K, int N, int* tile, int* splits) {
   if (!*splits) *splits = bs;
 }
 
-size_t prefill_workspace_bytes(int M, int N, int splits) {
+size_t prefill_workspace_bytes(int M, int N, int splits, bool gated) {
+  (void)gated;  // the gated epilogue needs the workspace only when K is split
   return splits > 1 ? (size_t)splits * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
 bool prefill_fits(int K, int N) { return (size_t)((N + 15) / 16) * ((K + 127) / 128) * 1024 < ((size_t)1 << 31); }
 
-hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, const Launch& L) {
+hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L) {
   if (!prefill_fits(a.K, a.N)) return hipErrorInvalidValue;
   if (splits > 1 && !ws) return hipErrorInvalidValue;
+  if (gated && a.N % 32) return hipErrorInvalidValue;
   switch (tile) {
-    case 1: return launch_prefill_k<2, 2, 4, 4, 64>(a, splits, ws, L);   // 128 x 128, 4 waves of 64 x 64, 64-row steps
-    case 2: return launch_prefill_k<2, 2, 4, 4, 128>(a, splits, ws, L);  // 128 x 128, 4 waves of 64 x 64, 128-row steps
-    case 3: return launch_prefill_k<2, 4, 8, 4, 128>(a, splits, ws, L);  // 256 x 256, 8 waves of 128 x 64, 128-row steps
+    case 1: return launch_prefill_k<2, 2, 4, 4, 64>(a, splits, ws, gated, L);   // 128 x 128, 4 waves of 64 x 64, 64-row steps
+    case 2: return launch_prefill_k<2, 2, 4, 4, 128>(a, splits, ws, gated, L);  // 128 x 128, 4 waves of 64 x 64, 128-row steps
+    case 3: return launch_prefill_k<2, 4, 8, 4, 128>(a, splits, ws, gated, L);  // 256 x 256, 8 waves of 128 x 64, 128-row steps
   }
   return hipErrorInvalidValue;
 }
