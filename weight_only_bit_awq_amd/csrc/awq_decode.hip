@@ -154,19 +154,25 @@ __device__ __forceinline__ void decode_staged_body(const uint16_t* __restrict__ 
   }
   const int64_t band = (int64_t)NT * 64;
   const uint32_t srow = (uint32_t)N * 2u, zrow = (uint32_t)(N / 8) * 4u;
-  auto load_band = [&](BandBuf<TPW, GB::NG>& b, int kt) {
+  // Two groups per band (G = 64): lanes 0..31 load the first group's scale
+  // and zero word, lanes 32..63 (the same columns) the second's; a swap of
+  // the two half-waves at use gives every lane both (one load each instead
+  // of two).
+  constexpr int NL = GPT == 2 ? 1 : GB::NG;  // scale/zero entries loaded per band
+  auto load_band = [&](BandBuf<TPW, NL>& b, int kt) {
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
 #pragma unroll
-      for (int gi = 0; gi < GB::NG; ++gi) {
-        const uint32_t g = min(GB::group(kt, gi, tpg), (uint32_t)groups - 1u);
+      for (int gi = 0; gi < NL; ++gi) {
+        const uint32_t g = GPT == 2 ? min((uint32_t)(2 * kt) + (uint32_t)(lane >> 5), (uint32_t)groups - 1u)
+                                    : min(GB::group(kt, gi, tpg), (uint32_t)groups - 1u);
         b.s[tt][gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[tt] + g * srow, 0, 0);
         b.zw[tt][gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[tt] + g * zrow, 0, 0);
       }
       b.wq[tt] = load_weights(qcol[tt] + kt * band);
     }
   };
-  BandBuf<TPW, GB::NG> buf[DEPTH];
+  BandBuf<TPW, NL> buf[DEPTH];
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) load_band(buf[d], min(w + WK * d, last));
 
@@ -189,15 +195,24 @@ __device__ __forceinline__ void decode_staged_body(const uint16_t* __restrict__ 
   for (int tt = 0; tt < TPW; ++tt) acc[tt] = f4{0.f, 0.f, 0.f, 0.f};
 
   const int lcol = lane & 15;  // column within a tile (16-column tiles start at multiples of 8)
-  auto consume = [&](const BandBuf<TPW, GB::NG>& b, int kt, float valid) {
+  auto consume = [&](const BandBuf<TPW, NL>& b, int kt, float valid) {
     h8 a[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) a[j] = *reinterpret_cast<const h8*>(xrow + 256 * kt + 64 * j);
 #pragma unroll
     for (int tt = 0; tt < TPW; ++tt) {
+      uint32_t sv[GB::NG], zv[GB::NG];
+      if constexpr (GPT == 2) {
+        const auto sp = __builtin_amdgcn_permlane32_swap(b.s[tt][0], b.s[tt][0], false, false);
+        const auto zp = __builtin_amdgcn_permlane32_swap(b.zw[tt][0], b.zw[tt][0], false, false);
+        sv[0] = sp[0], sv[1] = sp[1], zv[0] = zp[0], zv[1] = zp[1];
+      } else {
+#pragma unroll
+        for (int gi = 0; gi < GB::NG; ++gi) sv[gi] = b.s[tt][gi], zv[gi] = b.zw[tt][gi];
+      }
 #pragma unroll
       for (int gi = 0; gi < GB::NG; ++gi) {
-        const ZeroConst zc = zero_const(zero_nibble(b.zw[tt][gi], lcol));
+        const ZeroConst zc = zero_const(zero_nibble(zv[gi], lcol));
         f4 accg;
 #pragma unroll
         for (int jj = 0; jj < GB::JPG; ++jj) {
@@ -205,7 +220,7 @@ __device__ __forceinline__ void decode_staged_body(const uint16_t* __restrict__ 
           accg = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[j], decode_diff_vk(b.wq[tt][j], zc, kc),
                                                         jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg, 0, 0, 0);
         }
-        acc[tt] += (valid * scale_of(b.s[tt][gi])) * accg;
+        acc[tt] += (valid * scale_of(sv[gi])) * accg;
       }
     }
   };
