@@ -540,6 +540,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-g64", action="store_true", help="skip the group-64 (Falcon-7B) decode stack")
+    ap.add_argument("--no-gated", action="store_true", help="skip the gated-epilogue comparison")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -639,14 +640,16 @@ def main():
         torch.cuda.empty_cache()
 
     # Gated epilogue (silu(gate) * up) on the fused gate+up layer.
-    gated = {"what": "awq_linear_silu_mul (silu(gate) * up in the kernel's epilogue) against awq_linear "
-                     "followed by torch silu and multiply on the halves",
-             "decode_llama2_7b_gate_up_M1": gated_times(awq, lib, torch, hip, 4096, 22016, 128, 1, dev, 24, 4)}
-    if not args.no_prefill:
-        gated["prefill_llama2_13b_gate_up_M2048"] = gated_times(awq, lib, torch, hip, 5120, 27648, 128, 2048, dev,
-                                                                  2, 10)
-    eprint("[bench] gated: " + ", ".join(f"{k}: fused {v['fused_us']}us vs unfused {v['unfused_us']}us"
-                                          for k, v in gated.items() if isinstance(v, dict)))
+    gated = None
+    if not args.no_gated:
+        gated = {"what": "awq_linear_silu_mul (silu(gate) * up in the kernel's epilogue) against awq_linear "
+                         "followed by torch silu and multiply on the halves",
+                 "decode_llama2_7b_gate_up_M1": gated_times(awq, lib, torch, hip, 4096, 22016, 128, 1, dev, 24, 4)}
+        if not args.no_prefill:
+            gated["prefill_llama2_13b_gate_up_M2048"] = gated_times(awq, lib, torch, hip, 5120, 27648, 128, 2048,
+                                                                      dev, 2, 10)
+        eprint("[bench] gated: " + ", ".join(f"{k}: fused {v['fused_us']}us vs unfused {v['unfused_us']}us"
+                                              for k, v in gated.items() if isinstance(v, dict)))
 
     qt = quantize_times(awq, torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], wl.G, dev)
     qdom = max(qt, key=lambda k: qt[k]["median_us"])

@@ -288,9 +288,9 @@ __global__ __launch_bounds__(64 * WAVES) void decode_staged_kernel(const uint16_
   decode_staged_body<TM, GPT, WAVES, DEPTH, S>(x, qw, scales, zeros, y, M, K, N, G, NT, lay);
 }
 
-// The same kernel held to 64 VGPRs, i.e. eight waves per SIMD: used where
-// that costs no spills (one tile per wave, one group per band), so that four
-// 8-wave (or two 16-wave) workgroups fit on a CU.
+// The same kernel held to 64 VGPRs, i.e. eight waves per SIMD, so that four
+// 8-wave (or two 16-wave) workgroups fit on a CU; used only for the
+// instantiations that compile without spills (see launch_staged_s).
 template <int TM, int GPT, int WAVES, int DEPTH, int S>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(8))) void decode_staged_kernel_o8(
     const uint16_t* __restrict__ x, const u4* __restrict__ qw, const uint16_t* __restrict__ scales,
@@ -507,7 +507,9 @@ hipError_t launch_staged_k(F k, const LinearArgs& a, const StagedSizes& z, const
 
 template <int TM, int GPT, int WAVES, int S>
 hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
-  if constexpr (TM != 2 && GPT == 1)
+  // the 64-VGPR build only where it compiles without spills: one group per
+  // band, at most two 16-byte staging loads per thread, four or more waves
+  if constexpr (TM != 2 && GPT == 1 && S <= 2 && WAVES >= 4)
     return launch_staged_k<TM, WAVES>(decode_staged_kernel_o8<TM, GPT, WAVES, kStagedDepth, S>, a, z, L);
   else
     return launch_staged_k<TM, WAVES>(decode_staged_kernel<TM, GPT, WAVES, kStagedDepth, S>, a, z, L);
