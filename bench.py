@@ -335,6 +335,25 @@ def gated_times(awq, lib, torch, hip, K, N, G, M, dev, copies, reps):
     return out
 
 
+def decode_sweep(awq, lib, torch, hip, wl, dev, seed, layers=8, reps=3):
+    """Batched decode on the LLaMA-3-8B-shaped layers: for each M, the four
+    shapes' kernels (events at their own start and end) over `layers` copies
+    of each, cold weights; weight GB/s and TFLOP/s of one layer's four calls."""
+    out = {}
+    for M in wl.Ms:
+        stack, _ = build_stack(awq, torch, wl, M, dev, seed, layers=layers)
+        t = per_kernel_times(lib, torch, hip, stack, reps)
+        layer_ms = sum(sum(v) / len(v) for v in t.values())
+        wb = sum(weight_set_bytes(sh.K, sh.N, wl.G) for sh in wl.shapes)
+        fl = sum(2.0 * M * sh.K * sh.N for sh in wl.shapes)
+        out[f"M={M}"] = {"layer_us": round(layer_ms * 1e3, 2), "weight_GBps": round(wb / (layer_ms / 1e3) / 1e9, 1),
+                         "TFLOPs": round(fl / (layer_ms / 1e3) / 1e12, 2),
+                         "plans": {sh.name: awq.linear_plan(M, sh.K, sh.N, wl.G) for sh in wl.shapes}}
+        del stack
+        torch.cuda.empty_cache()
+    return out
+
+
 def quantize_times(awq, torch, shapes, G, dev, reps=10):
     """awq_quantize (fp16 W -> device qweight, scales, zeros) on each shape;
     HBM bytes per call = 2 B per weight read + the quantised weight set
@@ -541,6 +560,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-g64", action="store_true", help="skip the group-64 (Falcon-7B) decode stack")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-epilogue comparison")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the batched-decode sweep (M = 1 .. 32)")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -638,6 +658,15 @@ def main():
                ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s" for k, v in gps.items()))
         glayers = None
         torch.cuda.empty_cache()
+
+    # Batched decode: M = 1 .. 32 on the LLaMA-3-8B-shaped layers.
+    sweep = None
+    if not args.no_sweep:
+        ws3 = synth.LLAMA3_8B_SWEEP
+        sweep = {"workload": ws3.name, "group": ws3.G, "per_M": decode_sweep(awq, lib, torch, hip, ws3, dev,
+                                                                             args.seed + 3)}
+        eprint("[bench] decode sweep: " + ", ".join(f"{k} {v['layer_us']}us {v['weight_GBps']}GB/s"
+                                                    for k, v in sweep["per_M"].items()))
 
     # Gated epilogue (silu(gate) * up) on the fused gate+up layer.
     gated = None
@@ -745,6 +774,7 @@ def main():
         "roofline": roofline,
         "fp16_dense_reference": fp16_ref,
         "decode_g64": g64,
+        "decode_sweep": sweep,
         "gated": gated,
         "quantize": quantize,
         "prefill": prefill,

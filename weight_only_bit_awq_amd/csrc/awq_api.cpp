@@ -64,7 +64,13 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       p.tile < 0 || p.tile > 3)
     return AWQ_ERR_PLAN;
   if (gated && N % 32) return AWQ_ERR_SHAPE;
-  if (p.path == 0) p.path = gated ? (gated_decode_fits(M, K, G, p) ? 1 : 2) : (M <= kDecodeMaxM) ? 1 : 2;
+  // Automatic path: decode up to M = 64, except wide layers above M = 16,
+  // where the prefill GEMM streams the weights faster than the decode
+  // kernel re-reading activations per band (LLaMA-3-8B gate+up, M = 32:
+  // 48 against 62 us).
+  if (p.path == 0)
+    p.path = gated ? (gated_decode_fits(M, K, G, p) ? 1 : 2)
+                   : (M <= kDecodeMaxM && !(M > 16 && (N + 15) / 16 > 1024)) ? 1 : 2;
   if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
   if (p.path == 1 && gated && !gated_decode_fits(M, K, G, p)) return AWQ_ERR_PLAN;
   const int64_t KT = (K + 127) / 128;
@@ -97,10 +103,18 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
-    // long K: sixteen waves stage twice as much per pass
-    if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw) &&
-        awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
-      waves = 16;
+    // Activations too large to stage with these waves: sixteen waves stage
+    // twice as much per pass, but a 1024-thread workgroup with that much
+    // LDS holds a whole CU, so only where there are few workgroups (or one
+    // activation row, the long-K layers of Falcon-180B); otherwise the
+    // streamed variant, with four waves (measured on the LLaMA-3-8B layers,
+    // M = 4 .. 32).
+    if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw)) {
+      if ((M <= 2 || NT <= 512) && awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
+        waves = 16;
+      else
+        waves = 4;
+    }
     const bool fits = M >= 1 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
     if (x_stage == 0) x_stage = fits ? 1 : 2;
     if (x_stage == 1 && !fits) return AWQ_ERR_PLAN;
