@@ -131,8 +131,9 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
  *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
  *            the K range of the workgroup's 16 columns and their partial sums
  *            are added through LDS in a fixed order.
- *   tpw:     decode path, staged activations: 16-column tiles per workgroup
- *            (1 or 2).
+ *   tpw:     decode path: 16-column tiles per workgroup: 1 or 2 with staged
+ *            activations; 1, 2 or 4 with streamed activations (M <= 32, 4 or
+ *            8 waves), where each wave's activation loads serve all of them.
  *   x_stage: decode path: 1 = activations and the (scale, zero point) words
  *            of the workgroup's columns staged in LDS once per workgroup
  *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,

@@ -46,6 +46,9 @@ def test_decode_path(awq, M, K, N, G):
     plans = [{"path": 1}]
     for waves in (1, 2, 4, 8, 16):
         plans.append({"path": 1, "waves": waves, "x_stage": 2})
+        if waves in (4, 8):
+            for tpw in (2, 4):
+                plans.append({"path": 1, "waves": waves, "x_stage": 2, "tpw": tpw})
         for tpw in (1, 2):
             plans.append({"path": 1, "waves": waves, "x_stage": 1, "tpw": tpw})
     ran = 0

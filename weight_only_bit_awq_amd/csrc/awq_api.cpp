@@ -64,13 +64,12 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       p.tile < 0 || p.tile > 3)
     return AWQ_ERR_PLAN;
   if (gated && N % 32) return AWQ_ERR_SHAPE;
-  // Automatic path: decode up to M = 64, except wide layers above M = 16,
-  // where the prefill GEMM streams the weights faster than the decode
-  // kernel re-reading activations per band (LLaMA-3-8B gate+up, M = 32:
-  // 48 against 62 us).
+  // Automatic path: decode up to M = 64, except wide layers above M = 32,
+  // where the prefill GEMM streams the weights faster than a decode kernel
+  // that re-reads the activations per band and tile.
   if (p.path == 0)
     p.path = gated ? (gated_decode_fits(M, K, G, p) ? 1 : 2)
-                   : (M <= kDecodeMaxM && !(M > 16 && (N + 15) / 16 > 1024)) ? 1 : 2;
+                   : (M <= kDecodeMaxM && !(M > 32 && (N + 15) / 16 > 1024)) ? 1 : 2;
   if (p.path == 1 && M > kDecodeMaxM) return AWQ_ERR_PLAN;
   if (p.path == 1 && gated && !gated_decode_fits(M, K, G, p)) return AWQ_ERR_PLAN;
   const int64_t KT = (K + 127) / 128;
@@ -90,7 +89,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (p.split_k > 1) return AWQ_ERR_PLAN;
     if (p.waves && p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8 && p.waves != 16)
       return AWQ_ERR_PLAN;
-    if (p.tpw > 2) return AWQ_ERR_PLAN;
+    if (p.tpw > 4 || p.tpw == 3) return AWQ_ERR_PLAN;
     // Automatic choice (measured on the LLaMA-shaped decode layers, M = 1):
     // one 16-column tile per workgroup and eight waves splitting K, unless
     // that makes more than about 12k waves (very wide layers: four), or the
@@ -103,23 +102,37 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
-    // Activations too large to stage with these waves: sixteen waves stage
-    // twice as much per pass, but a 1024-thread workgroup with that much
-    // LDS holds a whole CU, so only where there are few workgroups (or one
-    // activation row, the long-K layers of Falcon-180B); otherwise the
-    // streamed variant, with four waves (measured on the LLaMA-3-8B layers,
-    // M = 4 .. 32).
-    if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw)) {
-      if ((M <= 2 || NT <= 512) && awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
+    if (!gated && !p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
+      // Batched rows on layers of 384 or more tiles: the streamed variant,
+      // with adjacent tiles sharing each band's activation loads, beats
+      // staging the activations per workgroup (measured on the LLaMA-3-8B
+      // layers, M = 4 .. 32: e.g. QKV at M = 8, 5.9 against 11.6 us).
+      x_stage = 2;
+      if (!p.waves) waves = 4;
+    } else if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw)) {
+      // Activations too large to stage with these waves: sixteen waves
+      // stage twice as much per pass, but a 1024-thread workgroup with that
+      // much LDS holds a whole CU, so only where there are few workgroups (or
+      // one activation row, the long-K layers of Falcon-180B); otherwise the
+      // streamed variant with four waves.
+      if ((M <= 2 || NT <= 256) && awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
         waves = 16;
       else
         waves = 4;
     }
-    const bool fits = M >= 1 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
+    const bool fits = M >= 1 && p.tpw <= 2 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
     if (x_stage == 0) x_stage = fits ? 1 : 2;
     if (x_stage == 1 && !fits) return AWQ_ERR_PLAN;
-    if (x_stage == 2) tpw = 1;
-    if (x_stage == 2 && p.tpw > 1) return AWQ_ERR_PLAN;
+    if (x_stage == 2) {
+      // Streamed: up to four adjacent tiles per workgroup share each band's
+      // activation loads (M <= 32, four or eight waves); automatic: four
+      // from 1024 tiles, two from 384.
+      const bool multi = M <= 32 && (waves == 4 || waves == 8);
+      if (p.tpw > 1 && !multi) return AWQ_ERR_PLAN;
+      // (four tiles of 32 rows with four groups per band hold too many
+      // registers: two there)
+      tpw = p.tpw ? p.tpw : !multi ? 1 : (NT >= 1024 && (M <= 16 || G >= 64)) ? 4 : NT >= 384 ? 2 : 1;
+    }
     if (p.tile) return AWQ_ERR_PLAN;
     out->waves = waves;
     out->tpw = tpw;

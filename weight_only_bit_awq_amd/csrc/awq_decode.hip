@@ -303,34 +303,38 @@ __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(8)))
 // Streamed variant
 // ---------------------------------------------------------------------------
 
-template <int MT, int GPT>
+template <int MT, int GPT, int TW>
 struct Bundle {
-  u4 wq;                                // one 16-byte slice of the tile: 4 words
-  u4 xa[MT][4];                         // A operand per 32-row block and 16-row tile
-  uint32_t s[GroupsPerBand<GPT>::NG];   // scale bits per group entry
-  uint32_t zw[GroupsPerBand<GPT>::NG];  // packed zero-point word per group entry
+  u4 wq[TW];                                // one 16-byte slice of each tile: 4 words
+  u4 xa[MT][4];                             // A operand per 32-row block and 16-row tile
+  uint32_t s[TW][GroupsPerBand<GPT>::NG];   // scale bits per tile and group entry
+  uint32_t zw[TW][GroupsPerBand<GPT>::NG];  // packed zero-point word per tile and group entry
 };
 
+template <int TW>
 struct StreamCtx {
   rsrc_t rx, rs, rz;
-  const u4* qcol;       // this lane's slice of its column tile in band 0
-  int64_t band;         // u4 stride between bands
-  uint32_t xoff[4];     // per 16-row tile: byte offset of (row, 8h) or kOOB
-  uint32_t soff, zoff;  // byte offsets of this lane's scale / zero word, or kOOB
-  uint32_t srow, zrow;  // bytes per group row of scales / zeros
+  const u4* qcol[TW];       // this lane's slice of each column tile in band 0
+  int64_t band;             // u4 stride between bands
+  uint32_t xoff[4];         // per 16-row tile: byte offset of (row, 8h) or kOOB
+  uint32_t soff[TW], zoff[TW];  // byte offsets of this lane's scale / zero word, or kOOB
+  uint32_t srow, zrow;      // bytes per group row of scales / zeros
   int tpg;
   int K;
 };
 
-template <int MT, int GPT>
-__device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const StreamCtx& c, int kt) {
+template <int MT, int GPT, int TW>
+__device__ __forceinline__ void load_bundle(Bundle<MT, GPT, TW>& b, const StreamCtx<TW>& c, int kt) {
   using GB = GroupsPerBand<GPT>;
-  b.wq = load_weights(c.qcol + kt * c.band);
 #pragma unroll
-  for (int gi = 0; gi < GB::NG; ++gi) {
-    const uint32_t g = GB::group(kt, gi, c.tpg);
-    b.s[gi] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, c.soff + g * c.srow, 0, 0);
-    b.zw[gi] = __builtin_amdgcn_raw_buffer_load_b32(c.rz, c.zoff + g * c.zrow, 0, 0);
+  for (int tt = 0; tt < TW; ++tt) {
+    b.wq[tt] = load_weights(c.qcol[tt] + kt * c.band);
+#pragma unroll
+    for (int gi = 0; gi < GB::NG; ++gi) {
+      const uint32_t g = GB::group(kt, gi, c.tpg);
+      b.s[tt][gi] = __builtin_amdgcn_raw_buffer_load_b16(c.rs, c.soff[tt] + g * c.srow, 0, 0);
+      b.zw[tt][gi] = __builtin_amdgcn_raw_buffer_load_b32(c.rz, c.zoff[tt] + g * c.zrow, 0, 0);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -344,116 +348,137 @@ __device__ __forceinline__ void load_bundle(Bundle<MT, GPT>& b, const StreamCtx&
   }
 }
 
-template <int MT, int GPT>
-__device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT>& b, f4 (&acc)[MT], int col, float valid,
-                                               const DecodeConsts& kc) {
+// The activation fragments of a band are loaded once and used for all TW
+// column tiles of the workgroup.
+template <int MT, int GPT, int TW>
+__device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT, TW>& b, f4 (&acc)[TW][MT], int col,
+                                               float valid, const DecodeConsts& kc) {
   using GB = GroupsPerBand<GPT>;
 #pragma unroll
-  for (int gi = 0; gi < GB::NG; ++gi) {
-    const ZeroConst zc = zero_const(zero_nibble(b.zw[gi], col));
-    f4 accg[MT];
+  for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
-    for (int jj = 0; jj < GB::JPG; ++jj) {
-      const int j = gi * GB::JPG + jj;
-      const h8 bw = decode_diff_vk(b.wq[j], zc, kc);
+    for (int gi = 0; gi < GB::NG; ++gi) {
+      const ZeroConst zc = zero_const(zero_nibble(b.zw[tt][gi], col));
+      f4 accg[MT];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.xa[mt][j]), bw,
-                                                          jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg[mt], 0, 0, 0);
+      for (int jj = 0; jj < GB::JPG; ++jj) {
+        const int j = gi * GB::JPG + jj;
+        const h8 bw = decode_diff_vk(b.wq[tt][j], zc, kc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8, b.xa[mt][j]), bw,
+                                                            jj == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg[mt], 0, 0, 0);
+      }
+      const float sf = valid * scale_of(b.s[tt][gi]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[tt][mt] += sf * accg[mt];
     }
-    const float sf = valid * scale_of(b.s[gi]);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] += sf * accg[mt];
-  }
 }
 
-template <int MT, int GPT, int WAVES, int DEPTH>
+// TW: 16-column tiles per workgroup (adjacent), each wave covering all of
+// them for its bands, so the activations it loads serve TW tiles.
+template <int MT, int GPT, int WAVES, int DEPTH, int TW>
 __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_t* __restrict__ x,
                                                                    const u4* __restrict__ qw,
                                                                    const uint16_t* __restrict__ scales,
                                                                    const uint32_t* __restrict__ zeros,
                                                                    uint16_t* __restrict__ y, int M, int K, int N,
                                                                    int G, int NT) {
-  const int t = xcd_remap(blockIdx.x, gridDim.x);
+  const int t0 = xcd_remap(blockIdx.x, gridDim.x) * TW;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 4;
-  const int col = 16 * t + (lane & 15);
   const int groups = K / G;
   const int KT = (K + 127) / 128;
 
-  StreamCtx c;
+  StreamCtx<TW> c;
   c.rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
   c.rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
   c.rz = make_rsrc(zeros, (uint32_t)groups * (uint32_t)(N / 8) * 4u);
-  c.qcol = qw + (int64_t)t * 64 + lane;
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) {
+    // tiles past the last one read the last tile's weights (never stored)
+    c.qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
+    const int col = 16 * (t0 + tt) + (lane & 15);
+    c.soff[tt] = col < N ? (uint32_t)col * 2u : kOOB;
+    c.zoff[tt] = col < N ? (uint32_t)(col >> 3) * 4u : kOOB;
+  }
   c.band = (int64_t)NT * 64;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
     const int row = 16 * mt + (lane & 15);
     c.xoff[mt] = row < M ? (uint32_t)(row * K + 8 * h) * 2u : kOOB;
   }
-  c.soff = col < N ? (uint32_t)col * 2u : kOOB;
-  c.zoff = col < N ? (uint32_t)(col >> 3) * 4u : kOOB;
   c.srow = (uint32_t)N * 2u;
   c.zrow = (uint32_t)(N / 8) * 4u;
   c.tpg = G / 128;
   c.K = K;
   const DecodeConsts kc = decode_consts();
+  const int lcol = lane & 15;
 
   const int n_my = KT > w ? (KT - w + WAVES - 1) / WAVES : 0;
   const int last = max(w + WAVES * (n_my - 1), 0);
 
-  f4 acc[MT];
+  f4 acc[TW][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[tt][mt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  Bundle<MT, GPT> buf[DEPTH];
+  Bundle<MT, GPT, TW> buf[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * d, last));
+  for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT, TW>(buf[d], c, min(w + WAVES * d, last));
   const int rounds = max((n_my + DEPTH - 1) / DEPTH, 1);
   for (int r = 0; r < rounds - 1; ++r) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int i = r * DEPTH + d;
-      consume_bundle<MT, GPT>(buf[d], acc, col, 1.f, kc);
-      load_bundle<MT, GPT>(buf[d], c, min(w + WAVES * (i + DEPTH), last));
+      consume_bundle<MT, GPT, TW>(buf[d], acc, lcol, 1.f, kc);
+      load_bundle<MT, GPT, TW>(buf[d], c, min(w + WAVES * (i + DEPTH), last));
     }
   }
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d) {
     const int i = (rounds - 1) * DEPTH + d;
-    consume_bundle<MT, GPT>(buf[d], acc, col, i < n_my ? 1.f : 0.f, kc);
+    consume_bundle<MT, GPT, TW>(buf[d], acc, lcol, i < n_my ? 1.f : 0.f, kc);
   }
 
-  // Sum the waves' partial tiles. Lane l, register r of 16-row tile mt holds
-  // output row 16mt + 4(l/16) + r, column 16t + l%16.
+  // Sum the waves' partial tiles, one column tile at a time. Lane l,
+  // register r of 16-row tile mt holds output row 16mt + 4(l/16) + r,
+  // column 16(t0 + tt) + l%16.
   if constexpr (WAVES > 1) {
     constexpr int OUTS = MT * 4 * 64;
     __shared__ float red[WAVES][OUTS];
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int tt = 0; tt < TW; ++tt) {
+      if (tt) __syncthreads();  // the previous tile's sums have been read
 #pragma unroll
-      for (int r = 0; r < 4; ++r) red[w][(mt * 4 + r) * 64 + lane] = acc[mt][r];
-    __syncthreads();
-    for (int o = threadIdx.x; o < OUTS; o += 64 * WAVES) {
-      float v = 0.f;
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-      for (int ww = 0; ww < WAVES; ++ww) v += red[ww][o];
-      const int ol = o & 63, mr = o >> 6;
-      const int row = 16 * (mr >> 2) + 4 * (ol >> 4) + (mr & 3);
-      const int cc = 16 * t + (ol & 15);
-      if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        for (int r = 0; r < 4; ++r) red[w][(mt * 4 + r) * 64 + lane] = acc[tt][mt][r];
+      __syncthreads();
+      for (int o = threadIdx.x; o < OUTS; o += 64 * WAVES) {
+        float v = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < WAVES; ++ww) v += red[ww][o];
+        const int ol = o & 63, mr = o >> 6;
+        const int row = 16 * (mr >> 2) + 4 * (ol >> 4) + (mr & 3);
+        const int cc = 16 * (t0 + tt) + (ol & 15);
+        if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+      }
     }
   } else {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
+    for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 16 * mt + 4 * h + r;
-        const float v = acc[mt][r];
-        if (row < M && col < N) y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
-      }
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * h + r;
+          const int col = 16 * (t0 + tt) + lcol;
+          const float v = acc[tt][mt][r];
+          if (row < M && col < N) y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
   }
 }
 
@@ -545,32 +570,44 @@ hipError_t launch_staged_t(const LinearArgs& a, int waves, const StagedSizes& z,
   return launch_staged_g<TM, 0>(a, waves, z, L);
 }
 
-template <int MT, int GPT, int WAVES>
-hipError_t launch_stream_t(const LinearArgs& a, const Launch& L) {
-  constexpr int DEPTH = MT == 1 ? 4 : (MT == 2 ? 3 : 2);
+template <int MT, int GPT, int WAVES, int TW>
+hipError_t launch_stream_k(const LinearArgs& a, const Launch& L) {
+  // bands in flight per wave: fewer when a band carries more registers
+  constexpr int DEPTH = TW == 1 ? (MT == 1 ? 4 : (MT == 2 ? 3 : 2)) : 2;
   const int NT = (a.N + 15) / 16;
-  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, DEPTH>, dim3((unsigned)NT), dim3(64 * WAVES), 0, L, a.x,
-                       reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, NT);
+  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, DEPTH, TW>, dim3((unsigned)((NT + TW - 1) / TW)),
+                       dim3(64 * WAVES), 0, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M,
+                       a.K, a.N, a.G, NT);
+}
+
+template <int MT, int GPT, int WAVES>
+hipError_t launch_stream_t(const LinearArgs& a, int tw, const Launch& L) {
+  if constexpr (MT <= 2 && (WAVES == 4 || WAVES == 8)) {
+    if (tw == 2) return launch_stream_k<MT, GPT, WAVES, 2>(a, L);
+    if (tw == 4) return launch_stream_k<MT, GPT, WAVES, 4>(a, L);
+  }
+  if (tw != 1) return hipErrorInvalidValue;
+  return launch_stream_k<MT, GPT, WAVES, 1>(a, L);
 }
 
 template <int MT, int GPT>
-hipError_t launch_stream_w(const LinearArgs& a, int waves, const Launch& L) {
+hipError_t launch_stream_w(const LinearArgs& a, int waves, int tw, const Launch& L) {
   switch (waves) {
-    case 1: return launch_stream_t<MT, GPT, 1>(a, L);
-    case 2: return launch_stream_t<MT, GPT, 2>(a, L);
-    case 4: return launch_stream_t<MT, GPT, 4>(a, L);
-    case 8: return launch_stream_t<MT, GPT, 8>(a, L);
-    case 16: return launch_stream_t<MT, GPT, 16>(a, L);
+    case 1: return launch_stream_t<MT, GPT, 1>(a, tw, L);
+    case 2: return launch_stream_t<MT, GPT, 2>(a, tw, L);
+    case 4: return launch_stream_t<MT, GPT, 4>(a, tw, L);
+    case 8: return launch_stream_t<MT, GPT, 8>(a, tw, L);
+    case 16: return launch_stream_t<MT, GPT, 16>(a, tw, L);
   }
   return hipErrorInvalidValue;
 }
 
 template <int MT>
-hipError_t launch_stream_g(const LinearArgs& a, int waves, const Launch& L) {
-  if (a.G == 32) return launch_stream_w<MT, 4>(a, waves, L);
-  if (a.G == 64) return launch_stream_w<MT, 2>(a, waves, L);
-  if (a.G == 128) return launch_stream_w<MT, 1>(a, waves, L);
-  return launch_stream_w<MT, 0>(a, waves, L);
+hipError_t launch_stream_g(const LinearArgs& a, int waves, int tw, const Launch& L) {
+  if (a.G == 32) return launch_stream_w<MT, 4>(a, waves, tw, L);
+  if (a.G == 64) return launch_stream_w<MT, 2>(a, waves, tw, L);
+  if (a.G == 128) return launch_stream_w<MT, 1>(a, waves, tw, L);
+  return launch_stream_w<MT, 0>(a, waves, tw, L);
 }
 
 }  // namespace
@@ -594,9 +631,9 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
     if (cfg.tpw == 2) return launch_staged_t<2>(a, cfg.waves, z, L);
     return launch_staged_t<1>(a, cfg.waves, z, L);
   }
-  if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, L);
-  if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, L);
-  if (a.M <= 64) return launch_stream_g<4>(a, cfg.waves, L);
+  if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, cfg.tpw, L);
+  if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, cfg.tpw, L);
+  if (a.M <= 64) return launch_stream_g<4>(a, cfg.waves, cfg.tpw, L);
   return hipErrorInvalidValue;
 }
 
