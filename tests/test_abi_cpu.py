@@ -133,6 +133,40 @@ def test_plans(lib):
     assert awq.linear_plan(512, 256, 5120, 128, {"path": 2, "tile": 2, "split_k": 8})["split_k"] == 2
 
 
+def test_batched_decode_plans(lib):
+    # the automatic choices measured on the LLaMA-3-8B layers (host logic only)
+    import weight_only_bit_awq_amd as awq
+    for K, N in [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]:
+        p1 = awq.linear_plan(1, K, N, 128)
+        assert p1["path"] == 1 and p1["x_stage"] == 1          # one row: staged activations
+    p = awq.linear_plan(8, 4096, 6144, 128)                     # 384 tiles: streamed, two tiles per workgroup
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 2, 4)
+    p = awq.linear_plan(32, 4096, 28672, 128)                   # 1792 tiles: four per workgroup
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 4, 4)
+    p = awq.linear_plan(32, 4096, 28672, 32)                    # 32-row groups at 32 rows: two
+    assert p["tpw"] == 2
+    p = awq.linear_plan(4, 14336, 4096, 128)                    # 256 tiles: staged, sixteen waves
+    assert (p["x_stage"], p["waves"]) == (1, 16)
+    assert awq.linear_plan(48, 4096, 28672, 128)["path"] == 2   # wide layer above 32 rows: GEMM
+    assert awq.linear_plan(48, 4096, 4096, 128)["path"] == 1
+    with pytest.raises(awq.AWQError):                           # four tiles only with streamed activations
+        awq.linear_plan(1, 4096, 4096, 128, {"path": 1, "tpw": 4, "x_stage": 1})
+    with pytest.raises(awq.AWQError):                           # and at most 32 rows
+        awq.linear_plan(40, 4096, 4096, 128, {"path": 1, "tpw": 2, "x_stage": 2})
+
+
+def test_gated_plans(lib):
+    import weight_only_bit_awq_amd as awq
+    p = awq.linear_silu_mul_plan(1, 4096, 22016, 128)           # fused decode kernel, gate/up waves halved
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 1, 1, 8)
+    assert awq.linear_silu_mul_plan(2048, 5120, 27648, 128)["path"] == 2
+    assert awq.linear_silu_mul_workspace_bytes(2048, 5120, 27648, 128) == 0
+    with pytest.raises(awq.AWQError):
+        awq.linear_silu_mul_plan(1, 4096, 22000, 128)            # N % 32 != 0
+    with pytest.raises(awq.AWQError):
+        awq.linear_silu_mul_plan(1, 4096, 22016, 128, {"path": 1, "waves": 1})
+
+
 def test_missing_library_raises(tmp_path, monkeypatch):
     import weight_only_bit_awq_amd as awq
     monkeypatch.setattr(awq, "_lib", None)

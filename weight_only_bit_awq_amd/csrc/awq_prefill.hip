@@ -117,8 +117,11 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   const int u = xcd_remap(blockIdx.x, gridDim.x);
   const int split = u / n_tiles;
   const int tile = u - split * n_tiles;
-  const int mtile = tile % n_mtiles;
-  const int ntile = tile / n_mtiles;
+  // column tiles fastest: the workgroups that run together on one XCD share
+  // one activation slab (measured 1-1.5% faster than rows fastest)
+  const int n_ntiles = n_tiles / n_mtiles;
+  const int mtile = tile / n_ntiles;
+  const int ntile = tile % n_ntiles;
   const int m0 = mtile * C::BM;
   const int n0 = ntile * C::BN;  // plain: first global column of the workgroup
   const int NO = N / 2;           // gated: columns per half
