@@ -160,6 +160,17 @@ def test_gated_plans(lib):
     p = awq.linear_silu_mul_plan(1, 4096, 22016, 128)           # fused decode kernel, gate/up waves halved
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 1, 1, 8)
     assert awq.linear_silu_mul_plan(2048, 5120, 27648, 128)["path"] == 2
+    # one or two rows: the staged fused kernel, with waves that let the
+    # activations fit; more rows: the streamed one with gate and up tiles
+    # paired; above 32 rows: the GEMM
+    p = awq.linear_silu_mul_plan(2, 4096, 28672, 128)
+    assert (p["path"], p["x_stage"], p["tpw"]) == (1, 1, 1)
+    for M, tw in ((4, 4), (8, 4), (16, 4), (32, 4)):
+        p = awq.linear_silu_mul_plan(M, 4096, 28672, 128)
+        assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, tw, 4), (M, p)
+    with pytest.raises(awq.AWQError):                            # two tile pairs need an even number per half
+        awq.linear_silu_mul_plan(8, 1024, 96, 128, {"path": 1, "x_stage": 2, "tpw": 4})
+    assert awq.linear_silu_mul_plan(40, 4096, 28672, 128)["path"] == 2
     assert awq.linear_silu_mul_workspace_bytes(2048, 5120, 27648, 128) == 0
     with pytest.raises(awq.AWQError):
         awq.linear_silu_mul_plan(1, 4096, 22000, 128)            # N % 32 != 0

@@ -40,6 +40,10 @@ def sampled(q, z, s, cols):
 
 @pytest.mark.parametrize("M,K,N,G,plan", [
     (1, 256, 64, 64, None), (4, 1216, 96, 64, None), (16, 512, 160, 32, None), (1, 2048, 2048, 128, None),
+    (2, 1024, 256, 128, None), (8, 4544, 192, 64, None), (32, 1024, 544, 128, None), (20, 640, 96, 32, None),
+    (4, 768, 64, 128, {"path": 1, "x_stage": 2, "waves": 8}), (3, 640, 64, 128, {"path": 1, "x_stage": 1}),
+    (16, 1024, 2048, 128, {"path": 1, "x_stage": 2, "tpw": 4}), (24, 1216, 128, 64, {"path": 1, "tpw": 4}),
+    (9, 512, 256, 32, {"path": 1, "x_stage": 2, "tpw": 4, "waves": 8}),
     (3, 768, 64, 128, {"path": 1, "waves": 4}), (1, 14336, 256, 128, None),
     (20, 512, 96, 128, None), (300, 1024, 544, 64, None), (130, 2304, 160, 256, {"path": 2, "split_k": 3}),
     (8, 640, 64, 128, {"path": 2}), (513, 640, 96, 128, {"path": 2, "tile": 3}),
@@ -95,8 +99,8 @@ def test_gated_errors(awq):
     with pytest.raises(awq.AWQError):
         awq.linear_silu_mul(x, qw, sd, zw, 48, 64)                 # N % 32 != 0
     with pytest.raises(awq.AWQError):
-        awq.linear_silu_mul_plan(20, 128, 64, 64, {"path": 1})     # no fused decode kernel above M = 16
-    assert awq.linear_silu_mul_plan(20, 128, 64, 64)["path"] == 2
+        awq.linear_silu_mul_plan(40, 128, 64, 64, {"path": 1})     # no fused decode kernel above M = 32
+    assert awq.linear_silu_mul_plan(40, 128, 64, 64)["path"] == 2
     assert awq.linear_silu_mul_workspace_bytes(1, 128, 64, 64) == 0
-    assert awq.linear_silu_mul_workspace_bytes(20, 128, 64, 64) == 0      # epilogue in registers
+    assert awq.linear_silu_mul_workspace_bytes(40, 128, 64, 64) == 0      # epilogue in registers
     assert awq.linear_silu_mul_workspace_bytes(130, 2304, 160, 256, {"path": 2, "split_k": 3}) == 3 * 130 * 160 * 4

@@ -50,11 +50,21 @@ constexpr int kDecodeMaxM = 64;
 // variant with the gate and up tiles paired in one workgroup exists (half of
 // its waves on each tile), so the automatic choice takes the prefill path
 // whenever that does not fit.
-bool gated_decode_fits(int64_t M, int64_t K, int G, const awq_plan& p) {
-  if (M < 1 || M > 16 || p.tpw > 1 || p.x_stage == 2 || p.waves == 1) return false;
+// Returns the number of waves the fused kernel uses (0 if it cannot run).
+int gated_decode_waves(int64_t M, int64_t K, int G, const awq_plan& p) {
+  if (M < 1 || M > 16 || p.tpw > 1 || p.x_stage == 2 || p.waves == 1 || p.waves == 2) return 0;
   for (int w : {8, 4, 16})
-    if ((!p.waves || p.waves == w) && awq::decode_staged_fits((int)M, (int)K, G, w, 1)) return true;
-  return false;
+    if ((!p.waves || p.waves == w) && awq::decode_staged_fits((int)M, (int)K, G, w, 1)) return w;
+  return 0;
+}
+// The streamed variant with the gate and up tiles sharing each band's
+// activation loads (M <= 32, four or eight waves).
+bool gated_stream_ok(int64_t M, const awq_plan& p) {
+  return M >= 1 && M <= 32 && (!p.waves || p.waves == 4 || p.waves == 8) && p.x_stage != 1 &&
+         (!p.tpw || p.tpw == 2 || p.tpw == 4);
+}
+bool gated_decode_fits(int64_t M, int64_t K, int G, const awq_plan& p) {
+  return gated_decode_waves(M, K, G, p) > 0 || gated_stream_ok(M, p);
 }
 
 int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out, bool gated = false) {
@@ -94,15 +104,33 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     // one 16-column tile per workgroup and eight waves splitting K, unless
     // that makes more than about 12k waves (very wide layers: four), or the
     // layer has fewer than 8 full 128-row bands.
+    if (gated) {
+      // Fused gate+up: the staged kernel (halves of its waves on the gate
+      // and the up tile) for one or two rows, else the streamed one with the
+      // two tiles sharing each band's activation loads.
+      if (p.tile) return AWQ_ERR_PLAN;
+      const int sw = gated_decode_waves(M, K, G, p);
+      const bool st = gated_stream_ok(M, p);
+      if (sw && (p.x_stage == 1 || M <= 2 || !st)) {
+        out->waves = sw, out->tpw = 1, out->x_stage = 1;
+      } else if (st) {
+        // tpw = tiles per workgroup, half gate and half up: four (two
+        // pairs) on wide layers, as for the plain layer
+        const int64_t NH = NT / 2;
+        int tw = p.tpw ? p.tpw : (NH >= 512 && NH % 2 == 0 && (M <= 16 || G >= 64)) ? 4 : 2;
+        if (tw == 4 && NH % 2) return AWQ_ERR_PLAN;
+        out->waves = p.waves ? p.waves : 4, out->tpw = tw, out->x_stage = 2;
+      } else {
+        return AWQ_ERR_PLAN;
+      }
+      return AWQ_OK;
+    }
     int waves = p.waves;
     if (!waves) waves = (NT * 8 > 12288 || KT < 8) ? 4 : 8;
-    // gated: the same waves per workgroup, half on the gate tile and half on
-    // the up tile (measured on the LLaMA-2-7B gate+up layer at M = 1: as
-    // fast as the plain layer's eight waves on one tile; sixteen are slower)
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
-    if (!gated && !p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
+    if (!p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
       // Batched rows on layers of 384 or more tiles: the streamed variant,
       // with adjacent tiles sharing each band's activation loads, beats
       // staging the activations per workgroup (measured on the LLaMA-3-8B

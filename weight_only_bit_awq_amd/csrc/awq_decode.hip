@@ -376,15 +376,21 @@ __device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT, TW>& b, f4 
 }
 
 // TW: 16-column tiles per workgroup (adjacent), each wave covering all of
-// them for its bands, so the activations it loads serve TW tiles.
-template <int MT, int GPT, int WAVES, int DEPTH, int TW>
+// them for its bands, so the activations it loads serve TW tiles. GATED (TW =
+// 2 or 4): TW/2 adjacent tiles of the gate half and the same tiles of the up
+// half, stored as y[m, n] = silu(gate) * up ([M, N/2]).
+template <int MT, int GPT, int WAVES, int DEPTH, int TW, bool GATED = false>
 __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_t* __restrict__ x,
                                                                    const u4* __restrict__ qw,
                                                                    const uint16_t* __restrict__ scales,
                                                                    const uint32_t* __restrict__ zeros,
                                                                    uint16_t* __restrict__ y, int M, int K, int N,
                                                                    int G, int NT) {
-  const int t0 = xcd_remap(blockIdx.x, gridDim.x) * TW;
+  static_assert(!GATED || TW == 2 || TW == 4, "gated: gate tiles and as many up tiles");
+  constexpr int TH = GATED ? TW / 2 : TW;  // gate tiles (gated) or tiles per workgroup
+  const int t0 = xcd_remap(blockIdx.x, gridDim.x) * TH;
+  // column tile of the workgroup's tile tt: the up tiles lie NT/2 after the gate tiles
+  auto tile_of = [&](int tt) { return GATED && tt >= TH ? NT / 2 + t0 + (tt - TH) : t0 + tt; };
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 4;
@@ -398,8 +404,8 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
 #pragma unroll
   for (int tt = 0; tt < TW; ++tt) {
     // tiles past the last one read the last tile's weights (never stored)
-    c.qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
-    const int col = 16 * (t0 + tt) + (lane & 15);
+    c.qcol[tt] = qw + (int64_t)min(tile_of(tt), NT - 1) * 64 + lane;
+    const int col = 16 * tile_of(tt) + (lane & 15);
     c.soff[tt] = col < N ? (uint32_t)col * 2u : kOOB;
     c.zoff[tt] = col < N ? (uint32_t)(col >> 3) * 4u : kOOB;
   }
@@ -446,7 +452,47 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
   // Sum the waves' partial tiles, one column tile at a time. Lane l,
   // register r of 16-row tile mt holds output row 16mt + 4(l/16) + r,
   // column 16(t0 + tt) + l%16.
-  if constexpr (WAVES > 1) {
+  if constexpr (GATED) {
+    // per gate tile: its sums and the up tile's, then silu(gate) * up
+    constexpr int OUTS = MT * 4 * 64;
+    constexpr int PER = (OUTS + 64 * WAVES - 1) / (64 * WAVES);  // outputs per thread
+    __shared__ float red[WAVES][OUTS];
+    const int NO = N / 2;
+#pragma unroll
+    for (int pt = 0; pt < TH; ++pt) {
+      float v[2][PER];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        if (pt || hf) __syncthreads();  // the previous sums have been read
+        const int tt = pt + hf * TH;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) red[w][(mt * 4 + r) * 64 + lane] = acc[tt][mt][r];
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int o = threadIdx.x + i * 64 * WAVES;
+          float a = 0.f;
+          if (o < OUTS) {
+#pragma unroll
+            for (int ww = 0; ww < WAVES; ++ww) a += red[ww][o];
+          }
+          v[hf][i] = a;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int o = threadIdx.x + i * 64 * WAVES;
+        const int ol = o & 63, mr = o >> 6;
+        const int row = 16 * (mr >> 2) + 4 * (ol >> 4) + (mr & 3);
+        const int cc = 16 * (t0 + pt) + (ol & 15);
+        const float g = v[0][i], u = v[1][i];
+        if (o < OUTS && row < M && cc < NO)
+          y[(int64_t)row * NO + cc] = __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + expf(-g)) * u));
+      }
+    }
+  } else if constexpr (WAVES > 1) {
     constexpr int OUTS = MT * 4 * 64;
     __shared__ float red[WAVES][OUTS];
 #pragma unroll
@@ -580,6 +626,32 @@ hipError_t launch_stream_k(const LinearArgs& a, const Launch& L) {
                        a.K, a.N, a.G, NT);
 }
 
+template <int MT, int GPT, int WAVES, int TW>
+hipError_t launch_stream_gated_k(const LinearArgs& a, const Launch& L) {
+  const int NT = (a.N + 15) / 16;
+  if ((NT / 2) % (TW / 2)) return hipErrorInvalidValue;  // whole groups of gate tiles
+  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, 2, TW, true>, dim3((unsigned)(NT / TW)),
+                       dim3(64 * WAVES), 0, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M,
+                       a.K, a.N, a.G, NT);
+}
+
+template <int MT, int GPT>
+hipError_t launch_stream_gated(const LinearArgs& a, int waves, int tw, const Launch& L) {
+  if (waves == 4 && tw == 2) return launch_stream_gated_k<MT, GPT, 4, 2>(a, L);
+  if (waves == 4 && tw == 4) return launch_stream_gated_k<MT, GPT, 4, 4>(a, L);
+  if (waves == 8 && tw == 2) return launch_stream_gated_k<MT, GPT, 8, 2>(a, L);
+  if (waves == 8 && tw == 4) return launch_stream_gated_k<MT, GPT, 8, 4>(a, L);
+  return hipErrorInvalidValue;
+}
+
+template <int MT>
+hipError_t launch_stream_gated_g(const LinearArgs& a, int waves, int tw, const Launch& L) {
+  if (a.G == 32) return launch_stream_gated<MT, 4>(a, waves, tw, L);
+  if (a.G == 64) return launch_stream_gated<MT, 2>(a, waves, tw, L);
+  if (a.G == 128) return launch_stream_gated<MT, 1>(a, waves, tw, L);
+  return launch_stream_gated<MT, 0>(a, waves, tw, L);
+}
+
 template <int MT, int GPT, int WAVES>
 hipError_t launch_stream_t(const LinearArgs& a, int tw, const Launch& L) {
   if constexpr (MT <= 2 && (WAVES == 4 || WAVES == 8)) {
@@ -620,9 +692,14 @@ bool decode_staged_fits(int M, int K, int G, int waves, int tpw) {
 
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L) {
   if (cfg.gated) {
-    // gate and up halves paired in one workgroup: needs the staged variant
-    if (!cfg.staged || a.N % 32 || cfg.waves < 2 || !decode_staged_fits(a.M, a.K, a.G, cfg.waves, 1))
+    // gate and up tiles paired in one workgroup
+    if (a.N % 32) return hipErrorInvalidValue;
+    if (!cfg.staged) {
+      if (a.M <= 16) return launch_stream_gated_g<1>(a, cfg.waves, cfg.tpw, L);
+      if (a.M <= 32) return launch_stream_gated_g<2>(a, cfg.waves, cfg.tpw, L);
       return hipErrorInvalidValue;
+    }
+    if (cfg.waves < 2 || !decode_staged_fits(a.M, a.K, a.G, cfg.waves, 1)) return hipErrorInvalidValue;
     return launch_staged_t<3>(a, cfg.waves, staged_sizes(a.M, a.K, a.G, cfg.waves, 1), L);
   }
   if (cfg.staged) {
