@@ -36,6 +36,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
 KERNEL_SOURCES = {
+    "quantize": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_quant.hip"),
     "decode": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_decode.hip"),
     "prefill": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_prefill.hip"),
 }
@@ -355,9 +356,9 @@ def decode_sweep(awq, lib, torch, hip, wl, dev, seed, layers=8, reps=3):
 
 
 def quantize_times(awq, torch, shapes, G, dev, reps=10):
-    """awq_quantize (fp16 W -> device qweight, scales, zeros) on each shape;
-    HBM bytes per call = 2 B per weight read + the quantised weight set
-    written. Returns {shape: {...}}."""
+    """awq_quantize (fp16 W -> device qweight, scales, zeros) on each shape,
+    per call from a graph of `reps` calls; HBM bytes per call = 2 B per
+    weight read + the quantised weight set written. Returns {shape: {...}}."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(77)
     out = {}
@@ -366,15 +367,28 @@ def quantize_times(awq, torch, shapes, G, dev, reps=10):
         for w in ws:
             awq.quantize(w, G)
         torch.cuda.synchronize()
+        # `reps` calls captured in a graph and replayed between two events:
+        # per-call time without the host's launch latency
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            awq.quantize(ws[0], G)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for r in range(reps):
+                awq.quantize(ws[r % 2], G)
+        torch.cuda.synchronize()
         ts = []
-        for r in range(reps):
+        for _ in range(3):
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record()
-            awq.quantize(ws[r % 2], G)
+            g.replay()
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
+            ts.append(e0.elapsed_time(e1) / reps)
+        del g
         ts.sort()
         med = ts[len(ts) // 2]
         nbytes = 2 * K * N + weight_set_bytes(K, N, G)
@@ -468,6 +482,14 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
             Mp = pw.Ms[0] if i < half else pw.Ms[1]
             sh = pw.shapes[(i if i < half else i - half) % len(pw.shapes)]
             out.setdefault(("prefill", f"{sh.name}@M={Mp}"), []).append(c)
+        # quantiser calls on the decode stack's shapes, told apart by their
+        # grid (one 256-thread workgroup per 128-row band and 128 columns)
+        qgrid = {((sh.N + 127) // 128) * ((sh.K + 127) // 128) * 256: sh.name for sh in synth.LLAMA2_7B_DECODE.shapes}
+        for r in seq:
+            if "quantize_" in r[0]:
+                name = qgrid.get(int(r[2].get("Grid_Size_X") or r[2].get("Grid_Size") or -1))
+                if name:
+                    out.setdefault(("quantize", name), []).append([r])
         return out
 
     trace = [(_short(r["Kernel_Name"]), None, r) for r in rows(trace_dir, "bench_kernel_trace.csv")
@@ -486,6 +508,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     pshape = {sh.name: sh for sh in synth.LLAMA2_13B_PREFILL.shapes}
 
     def alg_bytes(path, shape):
+        if path == "quantize":
+            sh = dshape[shape]
+            return 2 * sh.K * sh.N + weight_set_bytes(sh.K, sh.N, 128)
         if path == "decode":
             sh = dshape[shape]
             return weight_set_bytes(sh.K, sh.N, 128) + 2 * sh.K + 2 * sh.N
@@ -507,11 +532,11 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
               "| path | shape | kernels of one call | calls | kernel-trace us (median / min / max) | "
               "FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|---|---|---|---|"]
-    traffic = {"decode": {}, "prefill": {}}
+    traffic = {"decode": {}, "prefill": {}, "quantize": {}}
     for (path, shape), calls in sorted(dur.items()):
         per_call = [sum((int(r[2]["End_Timestamp"]) - int(r[2]["Start_Timestamp"])) / 1e3 for r in c)
                     for c in calls]
-        names = " + ".join(f"{r[0]} (grid {r[2]['Grid_Size_X']})" for r in calls[0])
+        names = " + ".join(f"{r[0]} (grid {r[2].get('Grid_Size_X') or r[2].get('Grid_Size')})" for r in calls[0])
         f_calls = fe.get((path, shape), [])
         w_calls = wr.get((path, shape), [])
         f_kib = statistics.mean(sum(float(r[2]["Counter_Value"]) for r in c) for c in f_calls) if f_calls else 0
@@ -527,7 +552,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     md = os.path.join(ROOT, "profiles", "decode_prefill_llama_bench.md")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    for path in ("decode", "prefill"):
+    for path in ("decode", "prefill", "quantize"):
         with open(os.path.join(ROOT, "profiles", f"{path}_traffic.json"), "w") as f:
             json.dump({"kernel_source_sha": source_sha(KERNEL_SOURCES[path]), "fetch_scale": ff,
                        "write_scale": fw, "shapes": traffic[path], "source": os.path.basename(md)}, f, indent=1)
@@ -673,7 +698,8 @@ def main():
     if not args.no_gated:
         gated = {"what": "awq_linear_silu_mul (silu(gate) * up in the kernel's epilogue) against awq_linear "
                          "followed by torch silu and multiply on the halves",
-                 "decode_llama2_7b_gate_up_M1": gated_times(awq, lib, torch, hip, 4096, 22016, 128, 1, dev, 24, 4)}
+                 "decode_llama2_7b_gate_up_M1": gated_times(awq, lib, torch, hip, 4096, 22016, 128, 1, dev, 24, 4),
+                 "decode_llama3_8b_gate_up_M16": gated_times(awq, lib, torch, hip, 4096, 28672, 128, 16, dev, 8, 4)}
         if not args.no_prefill:
             gated["prefill_llama2_13b_gate_up_M2048"] = gated_times(awq, lib, torch, hip, 5120, 27648, 128, 2048,
                                                                       dev, 2, 10)
@@ -687,6 +713,7 @@ def main():
                 "shapes": qt,
                 "roofline": {"bound": "hbm", "achieved": qt[qdom]["GBps"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                              "frac": round(qt[qdom]["GBps"] / HBM_PEAK_GBS, 4),
+                             "traffic": traffic_entry("quantize", qdom),
                              "kernel": f"quantize_kernel ({qdom})"}}
     eprint("[bench] quantize: " + ", ".join(f"{k} {v['median_us']}us {v['GBps']}GB/s" for k, v in qt.items()))
 
