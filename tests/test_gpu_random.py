@@ -1,0 +1,61 @@
+"""Seeded random shapes and plans through awq_linear and awq_linear_silu_mul:
+every plan the library accepts must meet the tolerance (any plan it rejects
+must be rejected before a launch, with AWQ_ERR_PLAN)."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.gpu_util import TOL, check_close, log, to_np16, upload_layer, x_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def awq():
+    import weight_only_bit_awq_amd as m
+    m.library()
+    return m
+
+
+def random_plan(rng):
+    if rng.random() < 0.3:
+        return None
+    if rng.random() < 0.6:
+        p = {"path": 1, "waves": int(rng.choice([0, 1, 2, 4, 8, 16])), "x_stage": int(rng.choice([0, 1, 2])),
+             "tpw": int(rng.choice([0, 1, 2, 4]))}
+    else:
+        p = {"path": 2, "tile": int(rng.choice([0, 1, 2, 3])), "split_k": int(rng.choice([0, 1, 2, 3, 7]))}
+    return p
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_shapes_and_plans(awq, seed):
+    rng = np.random.default_rng(1000 + seed)
+    G = int(rng.choice([32, 64, 128, 256]))
+    K = G * int(rng.integers(1, max(2, 2048 // G) + 1))
+    N = 32 * int(rng.integers(1, 20))
+    M = int(rng.choice([1, 2, 3, 5, 8, 13, 16, 17, 31, 33, 64, 65, 130, 257]))
+    gated = bool(rng.random() < 0.35)
+    plan = random_plan(rng)
+    planner = awq.linear_silu_mul_plan if gated else awq.linear_plan
+    try:
+        used = planner(M, K, N, G, plan)
+    except awq.AWQError as e:
+        assert e.status == -7, e  # only plan errors for valid shapes
+        log(f"random seed={seed} M={M} K={K} N={N} G={G} gated={gated} plan={plan}: rejected")
+        return
+    log(f"random seed={seed} M={M} K={K} N={N} G={G} gated={gated} plan={plan} -> {used}")
+    q, z, s = synth.layer(K, N, G, seed=seed)
+    x = synth.activations(M, K, seed=seed, outlier_frac=0.01 if K >= 100 else 0.0)
+    qw, zw, sd = upload_layer(q, z, s)
+    if gated:
+        y = to_np16(awq.linear_silu_mul(x_dev(x), qw, sd, zw, N, G, plan=plan)).astype(np.float64)
+        ref = oracle.linear_silu_mul64(x, q, z, s, G)
+        E = oracle.silu_mul_scale(x, q, z, s, G)
+        assert np.all(np.isfinite(y))
+        err = float(np.max(np.abs(y - ref)[E > 0] / E[E > 0]))
+        assert err <= TOL, err
+    else:
+        y = to_np16(awq.linear(x_dev(x), qw, sd, zw, N, G, plan=plan))
+        check_close(y, oracle.linear64(x, q, z, s, G), oracle.l1_scale(x, q, z, s, G), what=f"seed {seed}")
