@@ -33,6 +33,8 @@ SHAPES = [
     (17, 512, 136, 128), (33, 1024, 64, 64), (64, 640, 48, 128), (8, 11008, 128, 128), (2, 1024, 4104, 256),
     # ragged last band (K not a multiple of 128)
     (1, 4544, 72, 64), (4, 160, 24, 32), (9, 1216, 56, 64), (1, 32, 8, 32), (20, 1184, 40, 32),
+    # five 128-row bands per wave with eight waves (all in flight at once)
+    (1, 5120, 256, 128), (2, 4544, 64, 32),
 ]
 
 

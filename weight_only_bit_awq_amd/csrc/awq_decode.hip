@@ -578,6 +578,14 @@ hipError_t launch_staged_k(F k, const LinearArgs& a, const StagedSizes& z, const
 
 template <int TM, int GPT, int WAVES, int S>
 hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Launch& L) {
+  // Five bands per wave (e.g. K = 4544, 36 bands over 8 waves): all five in
+  // flight at once (measured on the Falcon-7B layers at group 64: QKV 6.9 ->
+  // 6.0 us), with the 64-VGPR build set aside (it would spill).
+  const int per_wave = ((a.K + 127) / 128 + WAVES - 1) / WAVES;
+  if constexpr (TM == 1) {
+    if (per_wave == 5)
+      return launch_staged_k<TM, WAVES>(decode_staged_kernel<TM, GPT, WAVES, 5, S>, a, z, L);
+  }
   // the 64-VGPR build only where it compiles without spills: one group per
   // band, at most two 16-byte staging loads per thread, four or more waves
   if constexpr (TM != 2 && GPT == 1 && S <= 2 && WAVES >= 4)
