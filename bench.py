@@ -107,6 +107,20 @@ class Layer:
         self.args = (x.data_ptr(), self.qw.data_ptr(), self.s.data_ptr(), self.zw.data_ptr(), self.M, K, N, G,
                      y.data_ptr(), self.ws_ptr, self.ws_len)
 
+    def rebound(self, awq, x, y, ws):
+        """The same weights with other activation / output buffers (M rows)."""
+        other = object.__new__(Layer)
+        other.__dict__.update(self.__dict__)
+        other.M = x.shape[0]
+        other.x, other.y = x, y
+        nbytes = awq.linear_workspace_bytes(other.M, self.K, self.N, self.G, self.plan)
+        buf = ws.get(nbytes) if nbytes else None
+        other.ws_ptr = buf.data_ptr() if buf is not None else None
+        other.ws_len = buf.numel() if buf is not None else 0
+        other.args = (x.data_ptr(), self.qw.data_ptr(), self.s.data_ptr(), self.zw.data_ptr(), other.M, self.K,
+                      self.N, self.G, y.data_ptr(), other.ws_ptr, other.ws_len)
+        return other
+
     def launch(self, lib, stream):
         st = lib.awq_linear_ex(*self.args, ctypes.byref(self.plan) if self.plan else None, stream)
         if st:
@@ -586,6 +600,7 @@ def main():
     ap.add_argument("--no-g64", action="store_true", help="skip the group-64 (Falcon-7B) decode stack")
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-epilogue comparison")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batched-decode sweep (M = 1 .. 32)")
+    ap.add_argument("--no-falcon180b", action="store_true", help="skip the 92 GB Falcon-180B-shaped stack")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -682,6 +697,33 @@ def main():
         eprint(f"[bench] G=64 stack: {gwall:.4f} ms/step, {g64['value']} GB/s; " +
                ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s" for k, v in gps.items()))
         glayers = None
+        torch.cuda.empty_cache()
+
+    # The Falcon-180B-shaped stack: 80 layers (92 GB of int4 weights) resident
+    # in HBM, one pass per step, at M = 1 and M = 16.
+    falcon = None
+    if not args.no_falcon180b:
+        wf = synth.FALCON_180B_STACK
+        eprint(f"[bench] building {wf.name}: {wf.layers} layers x {len(wf.shapes)} shapes")
+        flayers, fws = build_stack(awq, torch, wf, 1, dev, args.seed + 4)
+        fbytes = sum(weight_set_bytes(L.K, L.N, L.G) for _, L in flayers)
+        falcon = {"workload": wf.name, "layers": wf.layers, "group": wf.G, "weight_bytes_per_step": fbytes}
+        for Mf in wf.Ms:
+            if Mf == 1:
+                fl = flayers
+            else:
+                xs = {K: torch.randn((Mf, K), device=dev).half() for K in {L.K for _, L in flayers}}
+                ys = {N: torch.empty((Mf, N), dtype=torch.float16, device=dev) for N in {L.N for _, L in flayers}}
+                fl = [(n, L.rebound(awq, xs[L.K], ys[L.N], fws)) for n, L in flayers]
+            fwall, _ = time_stack_graph(lib, torch, fl, max(3, args.steps // 10), 2)
+            fps = per_shape_stats(awq, lib, torch, hip, wf, fl, Mf, 1)
+            falcon[f"M={Mf}"] = {"ms_per_step": round(fwall, 4), "weight_GBps": round(fbytes / (fwall / 1e3) / 1e9, 1),
+                                 "pct_hbm_peak": round(100 * fbytes / (fwall / 1e3) / 1e9 / HBM_PEAK_GBS, 2),
+                                 "per_kernel": fps}
+            eprint(f"[bench] {wf.name} M={Mf}: {fwall:.3f} ms/step, {falcon[f'M={Mf}']['weight_GBps']} GB/s; " +
+                   ", ".join(f"{k} {v['avg_us']}us {v['weight_GBps']}GB/s" for k, v in fps.items()))
+            fl = None
+        flayers = None
         torch.cuda.empty_cache()
 
     # Batched decode: M = 1 .. 32 on the LLaMA-3-8B-shaped layers.
@@ -802,6 +844,7 @@ def main():
         "fp16_dense_reference": fp16_ref,
         "decode_g64": g64,
         "decode_sweep": sweep,
+        "decode_falcon180b": falcon,
         "gated": gated,
         "quantize": quantize,
         "prefill": prefill,

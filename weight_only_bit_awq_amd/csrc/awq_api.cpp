@@ -117,7 +117,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
         // tpw = tiles per workgroup, half gate and half up: four (two
         // pairs) on wide layers, as for the plain layer
         const int64_t NH = NT / 2;
-        int tw = p.tpw ? p.tpw : (NH >= 512 && NH % 2 == 0 && (M <= 16 || G >= 64)) ? 4 : 2;
+        int tw = p.tpw ? p.tpw : (NH >= 448 && NH % 2 == 0 && (M <= 16 || G >= 64)) ? 4 : 2;
         if (tw == 4 && NH % 2) return AWQ_ERR_PLAN;
         out->waves = p.waves ? p.waves : 4, out->tpw = tw, out->x_stage = 2;
       } else {
@@ -154,12 +154,13 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (x_stage == 2) {
       // Streamed: up to four adjacent tiles per workgroup share each band's
       // activation loads (M <= 32, four or eight waves); automatic: four
-      // from 1024 tiles, two from 384.
+      // from 896 tiles (e.g. the Falcon-180B layers at M = 16: QKV 38.8 ->
+      // 29.6 us, down 140 -> 107 us), two from 384.
       const bool multi = M <= 32 && (waves == 4 || waves == 8);
       if (p.tpw > 1 && !multi) return AWQ_ERR_PLAN;
       // (four tiles of 32 rows with four groups per band hold too many
       // registers: two there)
-      tpw = p.tpw ? p.tpw : !multi ? 1 : (NT >= 1024 && (M <= 16 || G >= 64)) ? 4 : NT >= 384 ? 2 : 1;
+      tpw = p.tpw ? p.tpw : !multi ? 1 : (NT >= 896 && (M <= 16 || G >= 64)) ? 4 : NT >= 384 ? 2 : 1;
     }
     if (p.tile) return AWQ_ERR_PLAN;
     out->waves = waves;
