@@ -11,3 +11,6 @@ from .awq_oracle import (device_layout_doc, device_words, pack_canonical,  # noq
                          weight_set_bytes, model_bytes, low_nibble,
                          quantize_rtn, RTN_QMAX, silu64, linear_silu_mul64,
                          silu_mul_scale)
+from .attention_oracle import (ROPE_STYLES, rope_inv_freq64, rope_pairs, rope64,  # noqa: F401,E402
+                               split_qkv, softmax64, decode_step64, decode_error_scale,
+                               decode_bytes)
