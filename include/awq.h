@@ -63,7 +63,8 @@ enum awq_status {
   AWQ_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                 */
   AWQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required          */
   AWQ_ERR_HIP = -6,       /* the HIP runtime reported an error (see below)    */
-  AWQ_ERR_PLAN = -7       /* an explicit plan field is out of range           */
+  AWQ_ERR_PLAN = -7,      /* an explicit plan field is out of range           */
+  AWQ_ERR_ARG = -8        /* a scalar argument is out of range                */
 };
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -233,6 +234,86 @@ int awq_linear_silu_mul_workspace_bytes(int64_t M, int64_t K, int64_t N, int gro
  */
 int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
                     void* start_event, void* stop_event);
+
+/*
+ * Fused decode-step attention. "TinyChat: Efficient and Lightweight Chatbot
+ * with AWQ", section "Speed Benchmarks": in the generation stage every
+ * operation of multi-head, grouped-query and multi-query attention (MHA / GQA
+ * / MQA) runs in a single kernel, the positional embedding is fused into it,
+ * and the key-value caches are allocated up front. The pages define neither
+ * the attention nor the embedding; the readings taken are the textbook ones
+ * of the LLaMA and Falcon models in that section:
+ *
+ *   For each sequence b, with L = lengths[b] tokens already cached, the new
+ *   token's q, k, v are read from the QKV projection's output row qkv[b],
+ *   laid out as [Hq query heads | Hkv key heads | Hkv value heads] with D
+ *   values per head. q and k are rotated by the rotary embedding at position
+ *   L: pair i (i < D/2) turns counter-clockwise by L * theta^(-2i/D), the
+ *   pairs being (i, i + D/2) for AWQ_ROPE_HALF (LLaMA, Falcon) or (2i, 2i+1)
+ *   for AWQ_ROPE_INTERLEAVED; AWQ_ROPE_NONE leaves them as they are. Query
+ *   head h attends over the L cached keys of kv head h / (Hq / Hkv) and the
+ *   new key with softmax(scale * q . k), scale = softmax_scale (0: 1/sqrt(D)),
+ *   and out[b, h*D + d] = fp16(sum_j p_j v_j[d]). The rotated key, rounded
+ *   to fp16, and the value are written to slot L of the caches (the new token
+ *   attends to its key as stored).
+ *
+ * Arithmetic: rotation angles in fp64, rotations in fp32; products of fp16
+ * operands (q rounded to fp16, probabilities rounded to fp16 before the value
+ * product) summed in fp32; softmax in fp32 with the running maximum.
+ *
+ * Layouts (fp16 as uint16_t bits; device pointers, 16-byte aligned):
+ *   qkv      B rows of qkv_stride elements (>= (Hq + 2 Hkv) D, multiple of 8)
+ *   k_cache  [B, Hkv, capacity, D]: key element d of position j of (b, kv
+ *            head h) at ((b*Hkv + h)*capacity + j)*D + d
+ *   v_cache  [B, Hkv, D, capacity] (d-major): value element d of position j
+ *            at ((b*Hkv + h)*D + d)*capacity + j, so that the value product
+ *            reads consecutive positions
+ *   lengths  int32 [B]
+ *   out      [B, Hq*D]
+ * Sizes: D = 64 or 128; Hq a multiple of Hkv; capacity a multiple of 32 (at
+ * most 2^24); 0 <= max_cached < capacity. max_cached is a host-side bound on
+ * lengths[b]: the launch covers that many cached positions. A sequence whose
+ * lengths[b] is negative, above max_cached or not below capacity is skipped
+ * on the device: its output row is set to NaN and the caches keep their
+ * contents (the call still returns AWQ_OK).
+ * Workspace: awq_attention_workspace_bytes() bytes. The caller zero-fills it
+ * once when it is allocated; every call leaves it zero-filled again (it holds
+ * per-unit completion counters, which return to zero, and partial softmax
+ * states). Calls that share a workspace must not overlap (one stream).
+ * steps: 32-position blocks per wave (0: automatic); it sets how the cached
+ * positions are split over workgroups and changes only the summation order.
+ * B = 0 is a valid empty call.
+ */
+enum awq_rope_style { AWQ_ROPE_NONE = 0, AWQ_ROPE_HALF = 1, AWQ_ROPE_INTERLEAVED = 2 };
+
+typedef struct awq_attn_desc {
+  int64_t batch;         /* B                                                   */
+  int64_t q_heads;       /* Hq                                                  */
+  int64_t kv_heads;      /* Hkv (Hq % Hkv == 0; Hq == Hkv is MHA, Hkv == 1 MQA) */
+  int64_t head_dim;      /* D: 64 or 128                                        */
+  int64_t capacity;      /* cache slots per (sequence, kv head)                 */
+  int64_t max_cached;    /* host bound on lengths[b]                            */
+  int64_t qkv_stride;    /* elements between rows of qkv                        */
+  int32_t rope_style;    /* awq_rope_style                                      */
+  int32_t steps;         /* 0: automatic                                        */
+  float rope_theta;      /* base of the rotation rates (> 0 unless NONE)        */
+  float softmax_scale;   /* 0: 1/sqrt(D)                                        */
+} awq_attn_desc;
+
+int awq_attention_workspace_bytes(const awq_attn_desc* desc, size_t* bytes);
+/* The work split a call with `desc` uses: workgroups per unit (a unit is a
+ * sequence, kv head and tile of 16 query heads) and 32-position blocks per
+ * wave. Either pointer may be NULL. */
+int awq_attention_plan(const awq_attn_desc* desc, int32_t* workgroups_per_unit, int32_t* steps);
+int awq_attention_decode(const awq_attn_desc* desc, const uint16_t* qkv, uint16_t* k_cache,
+                         uint16_t* v_cache, const int32_t* lengths, uint16_t* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+/* awq_attention_decode with hipEvent_t handles recorded at the start and end
+ * of its kernel, as in awq_linear_timed (either may be NULL). */
+int awq_attention_decode_timed(const awq_attn_desc* desc, const uint16_t* qkv, uint16_t* k_cache,
+                               uint16_t* v_cache, const int32_t* lengths, uint16_t* out,
+                               void* workspace, size_t workspace_bytes, void* stream,
+                               void* start_event, void* stop_event);
 
 #ifdef __cplusplus
 }

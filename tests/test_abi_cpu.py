@@ -47,7 +47,7 @@ def test_binding_covers_header(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.awq_status_string(0) == b"AWQ_OK"
-    for code in range(-7, 0):
+    for code in range(-8, 0):
         assert lib.awq_status_string(code).startswith(b"AWQ_ERR")
     assert lib.awq_abi_version() == 1
 
@@ -192,3 +192,65 @@ def test_stream_read_validates_before_launch(lib):
     assert lib.awq_stream_read(None, 1024, ctypes.c_void_p(4096), None, None, None) == -1
     assert lib.awq_stream_read(ctypes.c_void_p(4096), 1000, ctypes.c_void_p(4096), None, None, None) == -2
     assert lib.awq_stream_read(ctypes.c_void_p(4104), 1024, ctypes.c_void_p(4096), None, None, None) == -4
+
+
+def _desc(**kw):
+    import weight_only_bit_awq_amd as awq
+    args = dict(B=1, q_heads=32, kv_heads=8, head_dim=128, capacity=4096, max_cached=4095)
+    args.update(kw)
+    return awq.attention_desc(args.pop("B"), args.pop("q_heads"), args.pop("kv_heads"), args.pop("head_dim"),
+                              args.pop("capacity"), args.pop("max_cached"), **args)
+
+
+def test_attention_validation_before_launch(lib):
+    import weight_only_bit_awq_amd as awq
+    sz = ctypes.c_size_t(0)
+
+    def ws(**kw):
+        return lib.awq_attention_workspace_bytes(ctypes.byref(_desc(**kw)), ctypes.byref(sz))
+
+    assert ws() == 0 and sz.value > 0
+    assert lib.awq_attention_workspace_bytes(None, ctypes.byref(sz)) == -1
+    assert ws(head_dim=96) == -2                       # D must be 64 or 128
+    assert ws(q_heads=30) == -2                        # Hq % Hkv
+    assert ws(capacity=40, max_cached=10) == -2        # capacity % 32
+    assert ws(max_cached=4096) == -2                   # max_cached < capacity
+    assert ws(qkv_stride=100) == -2                    # stride below the row width
+    assert ws(rope="half", theta=0.0) == -8            # theta > 0 with a rotation
+    assert ws(rope="none", theta=0.0) == 0             # ... not needed without
+    assert ws(scale=float("nan")) == -8
+    assert ws(steps=-1) == -7
+    d = _desc()
+    d.rope_style = 3
+    assert lib.awq_attention_workspace_bytes(ctypes.byref(d), ctypes.byref(sz)) == -8
+    # the launch entry point: empty batch is a no-op; NULL, alignment and
+    # workspace errors come back before anything is enqueued
+    A = ctypes.c_void_p(4096)
+    assert lib.awq_attention_decode(ctypes.byref(_desc(B=0)), None, None, None, None, None, None, 0, None) == 0
+    assert lib.awq_attention_decode(ctypes.byref(_desc()), None, A, A, A, A, A, 1 << 30, None) == -1
+    assert lib.awq_attention_decode(ctypes.byref(_desc()), ctypes.c_void_p(4104), A, A, A, A, A, 1 << 30,
+                                    None) == -4
+    need = awq.attention_workspace_bytes(_desc())
+    assert lib.awq_attention_decode(ctypes.byref(_desc()), A, A, A, A, A, A, need - 1, None) == -5
+    assert lib.awq_attention_decode(ctypes.byref(_desc()), A, A, A, A, A, ctypes.c_void_p(4096 + 16), need,
+                                    None) == -4
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,S,maxc,steps", [
+    (1, 32, 32, 128, 1024, 1023, 0), (1, 32, 8, 128, 4096, 4095, 0), (1, 71, 1, 64, 2048, 2047, 0),
+    (16, 32, 32, 128, 2048, 2047, 0), (3, 12, 4, 64, 64, 0, 0), (2, 8, 2, 128, 512, 300, 3),
+    (64, 32, 8, 128, 8192, 8000, 0)])
+def test_attention_plans_cover_the_cache(lib, B, Hq, Hkv, D, S, maxc, steps):
+    import weight_only_bit_awq_amd as awq
+    d = _desc(B=B, q_heads=Hq, kv_heads=Hkv, head_dim=D, capacity=S, max_cached=maxc, steps=steps)
+    pl = awq.attention_plan(d)
+    if steps:
+        assert pl["steps"] == steps
+    # four waves per workgroup, 32 positions per step: every cached position
+    # has a wave, and no workgroup starts past the bound
+    covered = pl["workgroups_per_unit"] * 4 * pl["steps"] * 32
+    assert covered >= max(maxc, 1) and covered - 4 * pl["steps"] * 32 < max(maxc, 1)
+    T = -(-(Hq // Hkv) // 16)
+    units = B * Hkv * T
+    nbytes = awq.attention_workspace_bytes(d)
+    assert nbytes >= -(-units * 4 // 256) * 256 + units * pl["workgroups_per_unit"] * 4 * 16 * (D + 4) * 4

@@ -40,6 +40,15 @@ class Plan(ctypes.Structure):
                 ("tpw", ctypes.c_int32), ("x_stage", ctypes.c_int32), ("tile", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("q_heads", ctypes.c_int64), ("kv_heads", ctypes.c_int64),
+                ("head_dim", ctypes.c_int64), ("capacity", ctypes.c_int64), ("max_cached", ctypes.c_int64),
+                ("qkv_stride", ctypes.c_int64), ("rope_style", ctypes.c_int32), ("steps", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("softmax_scale", ctypes.c_float)]
+
+
+ROPE_STYLES = {"none": 0, "half": 1, "interleaved": 2}
+
 _lib = None
 _lock = threading.Lock()
 
@@ -87,6 +96,16 @@ _SIGS = {
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "awq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_attention_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)]),
+    "awq_attention_plan": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_int32),
+                                          ctypes.POINTER(ctypes.c_int32)]),
+    "awq_attention_decode": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_size_t, ctypes.c_void_p]),
+    "awq_attention_decode_timed": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                                  ctypes.c_void_p, ctypes.c_void_p]),
 }
 
 
@@ -336,7 +355,105 @@ def linear_silu_mul(x, qweight, scales, zeros, N: int, group: int = 128, out=Non
     return out
 
 
-__all__ = ["library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_silu_mul",
+def attention_desc(B: int, q_heads: int, kv_heads: int, head_dim: int, capacity: int, max_cached: int,
+                   qkv_stride: int = 0, rope: str = "half", theta: float = 10000.0, scale: float = 0.0,
+                   steps: int = 0) -> AttnDesc:
+    """Descriptor of a fused decode-step attention call (see ``attention``)."""
+    if rope not in ROPE_STYLES:
+        raise ValueError(f"rope must be one of {sorted(ROPE_STYLES)}")
+    d = AttnDesc()
+    d.batch, d.q_heads, d.kv_heads, d.head_dim = B, q_heads, kv_heads, head_dim
+    d.capacity, d.max_cached = capacity, max_cached
+    d.qkv_stride = qkv_stride or (q_heads + 2 * kv_heads) * head_dim
+    d.rope_style, d.steps = ROPE_STYLES[rope], steps
+    d.rope_theta, d.softmax_scale = theta, scale
+    return d
+
+
+def attention_workspace_bytes(desc: AttnDesc) -> int:
+    out = ctypes.c_size_t()
+    _check(library().awq_attention_workspace_bytes(ctypes.byref(desc), ctypes.byref(out)))
+    return int(out.value)
+
+
+def attention_plan(desc: AttnDesc) -> dict:
+    c, s = ctypes.c_int32(), ctypes.c_int32()
+    _check(library().awq_attention_plan(ctypes.byref(desc), ctypes.byref(c), ctypes.byref(s)))
+    return {"workgroups_per_unit": int(c.value), "steps": int(s.value)}
+
+
+class AttentionWorkspace:
+    """Zero-filled device buffer for ``attention`` calls on one stream. The
+    kernel returns its counters to zero, so the buffer is filled once, when it
+    is allocated or grown."""
+
+    def __init__(self, device=None):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        torch = _torch()
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def kv_cache(B: int, kv_heads: int, capacity: int, head_dim: int, device=None):
+    """Zero-filled key cache [B, Hkv, capacity, D] and d-major value cache
+    [B, Hkv, D, capacity] (fp16) in the layouts ``attention`` reads."""
+    torch = _torch()
+    k = torch.zeros((B, kv_heads, capacity, head_dim), dtype=torch.float16, device=device)
+    v = torch.zeros((B, kv_heads, head_dim, capacity), dtype=torch.float16, device=device)
+    return k, v
+
+
+def attention(qkv, k_cache, v_cache, lengths, q_heads: int, kv_heads: int, max_cached=None, rope: str = "half",
+              theta: float = 10000.0, scale: float = 0.0, out=None, workspace=None, steps: int = 0, events=None):
+    """One generation step of attention with the rotary embedding fused in.
+
+    qkv [B, >= (Hq + 2 Hkv) D] fp16 (rows [q heads | k heads | v heads]),
+    k_cache [B, Hkv, S, D] and v_cache [B, Hkv, D, S] fp16 (updated in place:
+    slot lengths[b] receives the new rotated key and the value), lengths [B]
+    int32 on the device (tokens already cached). Returns out [B, Hq * D] fp16.
+    ``max_cached`` bounds lengths on the host (default S - 1)."""
+    torch = _torch()
+    _need(k_cache, torch.float16, "k_cache", 4)
+    _need(v_cache, torch.float16, "v_cache", 4)
+    _need(lengths, torch.int32, "lengths", 1)
+    if not isinstance(qkv, torch.Tensor) or qkv.dtype != torch.float16 or not qkv.is_cuda or qkv.dim() != 2:
+        raise TypeError("qkv must be a 2-D fp16 GPU tensor")
+    if qkv.stride(1) != 1:
+        raise ValueError("qkv rows must be contiguous")
+    B, Hkv, S, D = k_cache.shape
+    if Hkv != kv_heads or v_cache.shape != (B, Hkv, D, S):
+        raise ValueError("k_cache must be [B, Hkv, S, D] and v_cache [B, Hkv, D, S]")
+    if qkv.shape[0] != B or lengths.shape[0] != B or qkv.shape[1] < (q_heads + 2 * kv_heads) * D:
+        raise ValueError("qkv must be [B, >= (Hq + 2 Hkv) D] and lengths [B]")
+    desc = attention_desc(B, q_heads, kv_heads, D, S, S - 1 if max_cached is None else int(max_cached),
+                          qkv.stride(0) if B > 1 else qkv.shape[1] + (-qkv.shape[1]) % 8, rope, theta, scale,
+                          steps)
+    if out is None:
+        out = torch.empty((B, q_heads * D), dtype=torch.float16, device=qkv.device)
+    else:
+        _need(out, torch.float16, "out", 2)
+        if out.shape != (B, q_heads * D):
+            raise ValueError("out must be [B, Hq * D]")
+    nbytes = attention_workspace_bytes(desc)
+    if workspace is None:
+        workspace = AttentionWorkspace(qkv.device)
+    buf = workspace.get(nbytes) if isinstance(workspace, AttentionWorkspace) else workspace
+    lib = library()
+    args = (ctypes.byref(desc), qkv.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), lengths.data_ptr(),
+            out.data_ptr(), buf.data_ptr(), buf.numel() * buf.element_size(), _stream(qkv.device))
+    if events is None:
+        _check(lib.awq_attention_decode(*args))
+    else:
+        _check(lib.awq_attention_decode_timed(*args, events[0], events[1]))
+    return out
+
+
+__all__ = ["attention", "attention_desc", "attention_plan", "attention_workspace_bytes", "kv_cache",
+           "AttentionWorkspace", "library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_silu_mul",
            "linear_silu_mul_plan", "linear_silu_mul_workspace_bytes", "linear_plan",
            "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",
            "abi_version"]

@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
-SOURCES = ["awq_api.cpp", "awq_pack.hip", "awq_decode.hip", "awq_prefill.hip", "awq_probe.hip", "awq_quant.hip"]
+SOURCES = ["awq_api.cpp", "awq_pack.hip", "awq_decode.hip", "awq_prefill.hip", "awq_probe.hip", "awq_quant.hip",
+           "awq_attention.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

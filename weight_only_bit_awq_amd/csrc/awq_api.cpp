@@ -4,6 +4,7 @@
 // reports failures as negative status codes, never by throwing or aborting.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <math.h>
 #include <stdlib.h>
 
 #include "../../include/awq.h"
@@ -250,6 +251,66 @@ int workspace_out(int64_t M, int64_t K, int64_t N, int group, const awq_plan* pl
 
 }  // namespace
 
+namespace {
+
+// Attention: validation of the descriptor and the work split it implies.
+int attention_check(const awq_attn_desc* d, awq::AttnPlan* pl) {
+  if (!d) return AWQ_ERR_NULL;
+  if (d->batch < 0 || d->batch > (1 << 24) || d->q_heads < 1 || d->kv_heads < 1 || d->q_heads > 65536 ||
+      d->q_heads % d->kv_heads)
+    return AWQ_ERR_SHAPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return AWQ_ERR_SHAPE;
+  if (d->capacity < 32 || d->capacity % 32 || d->capacity > (1 << 24)) return AWQ_ERR_SHAPE;
+  if (d->max_cached < 0 || d->max_cached >= d->capacity) return AWQ_ERR_SHAPE;
+  if (d->qkv_stride < (d->q_heads + 2 * d->kv_heads) * d->head_dim || d->qkv_stride % 8) return AWQ_ERR_SHAPE;
+  if (d->rope_style < AWQ_ROPE_NONE || d->rope_style > AWQ_ROPE_INTERLEAVED) return AWQ_ERR_ARG;
+  if (d->rope_style != AWQ_ROPE_NONE && !(d->rope_theta > 0.f && d->rope_theta < INFINITY)) return AWQ_ERR_ARG;
+  if (!(d->softmax_scale >= 0.f && d->softmax_scale < INFINITY)) return AWQ_ERR_ARG;
+  if (d->steps < 0 || d->steps > 4096) return AWQ_ERR_PLAN;
+  *pl = awq::attention_plan((int)d->batch, (int)d->q_heads, (int)d->kv_heads, (int)d->head_dim,
+                            (int)d->max_cached, d->steps);
+  if ((int64_t)pl->C * pl->units > 0x7FFFFFFF) return AWQ_ERR_SHAPE;
+  return AWQ_OK;
+}
+
+int attention_run(const awq_attn_desc* d, const uint16_t* qkv, uint16_t* kc, uint16_t* vc, const int32_t* lengths,
+                  uint16_t* out, void* ws, size_t ws_bytes, const awq::Launch& L) {
+  awq::AttnPlan pl;
+  int st = attention_check(d, &pl);
+  if (st != AWQ_OK) return st;
+  if (d->batch == 0) return AWQ_OK;
+  if (!qkv || !kc || !vc || !lengths || !out) return AWQ_ERR_NULL;
+  if (!aligned(qkv, 16) || !aligned(kc, 16) || !aligned(vc, 16) || !aligned(out, 16) || !aligned(lengths, 4))
+    return AWQ_ERR_ALIGN;
+  if (!ws || ws_bytes < pl.ws_bytes) return AWQ_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return AWQ_ERR_ALIGN;
+  awq::AttnParams p;
+  p.qkv = qkv;
+  p.qkv_stride = d->qkv_stride;
+  p.kc = kc;
+  p.vc = vc;
+  p.lengths = lengths;
+  p.out = out;
+  p.counters = (uint32_t*)ws;
+  p.part = (float*)((char*)ws + pl.counter_bytes);
+  p.units = pl.units;
+  p.Hq = (int)d->q_heads;
+  p.Hkv = (int)d->kv_heads;
+  p.S = (int)d->capacity;
+  p.max_cached = (int)d->max_cached;
+  p.g = pl.g;
+  p.T = pl.T;
+  p.C = pl.C;
+  p.steps = pl.steps;
+  p.style = d->rope_style;
+  const double scale = d->softmax_scale > 0.f ? (double)d->softmax_scale : 1.0 / sqrt((double)d->head_dim);
+  p.scale_log2 = (float)(scale * 1.4426950408889634);
+  p.log2_theta = d->rope_style != AWQ_ROPE_NONE ? log2((double)d->rope_theta) : 0.0;
+  return hip_status(awq::launch_attention(p, (int)d->head_dim, L));
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* awq_status_string(int status) {
@@ -262,6 +323,7 @@ const char* awq_status_string(int status) {
     case AWQ_ERR_WORKSPACE: return "AWQ_ERR_WORKSPACE: workspace missing or too small";
     case AWQ_ERR_HIP: return "AWQ_ERR_HIP: the HIP runtime reported an error";
     case AWQ_ERR_PLAN: return "AWQ_ERR_PLAN: an explicit plan field is out of range";
+    case AWQ_ERR_ARG: return "AWQ_ERR_ARG: a scalar argument is out of range";
   }
   return "AWQ: unknown status";
 }
@@ -390,6 +452,38 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream, voi
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
                int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
   return awq_linear_ex(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+int awq_attention_workspace_bytes(const awq_attn_desc* desc, size_t* bytes) {
+  if (!bytes) return AWQ_ERR_NULL;
+  awq::AttnPlan pl;
+  const int st = attention_check(desc, &pl);
+  if (st != AWQ_OK) return st;
+  *bytes = desc->batch ? pl.ws_bytes : 0;
+  return AWQ_OK;
+}
+
+int awq_attention_plan(const awq_attn_desc* desc, int32_t* workgroups_per_unit, int32_t* steps) {
+  awq::AttnPlan pl;
+  const int st = attention_check(desc, &pl);
+  if (st != AWQ_OK) return st;
+  if (workgroups_per_unit) *workgroups_per_unit = pl.C;
+  if (steps) *steps = pl.steps;
+  return AWQ_OK;
+}
+
+int awq_attention_decode(const awq_attn_desc* desc, const uint16_t* qkv, uint16_t* k_cache, uint16_t* v_cache,
+                         const int32_t* lengths, uint16_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  const awq::Launch L{(hipStream_t)stream, nullptr, nullptr};
+  return attention_run(desc, qkv, k_cache, v_cache, lengths, out, workspace, workspace_bytes, L);
+}
+
+int awq_attention_decode_timed(const awq_attn_desc* desc, const uint16_t* qkv, uint16_t* k_cache,
+                               uint16_t* v_cache, const int32_t* lengths, uint16_t* out, void* workspace,
+                               size_t workspace_bytes, void* stream, void* start_event, void* stop_event) {
+  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return attention_run(desc, qkv, k_cache, v_cache, lengths, out, workspace, workspace_bytes, L);
 }
 
 }  // extern "C"

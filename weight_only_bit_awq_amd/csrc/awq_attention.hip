@@ -1,0 +1,334 @@
+// Fused decode-step attention: rotary position embedding, MHA / GQA / MQA
+// scaled dot-product attention over a pre-allocated fp16 key-value cache, and
+// the append of the new token's key and value, in one kernel launch.
+//
+// "TinyChat: Efficient and Lightweight Chatbot with AWQ", section "Speed
+// Benchmarks": in the generation stage all operations of MHA/GQA/MQA run in
+// a single kernel with the positional embedding fused into it, and the
+// key-value caches are allocated up front. Per generated token the step reads
+// every cached key and value once, so it is bound by HBM bandwidth.
+//
+// Design
+//   * Work unit = (sequence b, key/value head, tile of 16 query heads of that
+//     head's group). A workgroup of four waves takes one contiguous range of
+//     cached positions of one unit; each wave streams `steps` blocks of 32
+//     positions of its own sub-range with online softmax, and writes its
+//     partial state (running max, sum, unnormalised output) to the workspace.
+//   * Scores on the matrix cores: v_mfma_f32_16x16x32_f16 with the keys as the
+//     A operand (lane l loads 16 bytes of key row k(l%16) at d = 8(l/16) of
+//     each 32-wide d block) and the rotated queries as B. The key rows of a
+//     32-position block are ordered so that the score tile a lane receives
+//     (head l%16, four positions) is exactly the B operand of
+//     v_mfma_f32_16x16x16_f16 for the value product, and the values it needs
+//     (eight consecutive positions of one d row) are one 16-byte load from the
+//     d-major value cache. No cross-lane moves besides two max reductions.
+//   * The rotation angles are computed once per workgroup in fp64 (rate
+//     theta^(-2i/D) times the position), kept as fp32 cos/sin in LDS.
+//   * The last workgroup of a unit to finish (an agent-scope counter in the
+//     workspace, returned to zero by that workgroup) merges the partial states
+//     in a fixed order, adds the new token (its rotated key rounded to fp16,
+//     as it is stored, and its value), writes the fp16 output and, for the
+//     unit's first tile, appends the key and value to the caches.
+//   * Positions at or beyond a sequence's length are masked: their scores are
+//     replaced by -inf and their values by zero before the value product, so
+//     stale cache contents (even NaN patterns) never reach the output.
+#include <math.h>
+
+#include <algorithm>
+
+#include "awq_device.h"
+#include "awq_launch.h"
+
+namespace awq {
+
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+namespace {
+
+constexpr int kAttnWaves = 4;
+constexpr int kAttnBlock = 32;    // positions per wave step
+constexpr float kNoMax = -3.0e38f;  // running max before any position
+
+__device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
+__device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
+
+// DP consecutive fp16 values at `src` (aligned to their size) as fp32.
+template <int DP>
+__device__ __forceinline__ void load_halves(const uint16_t* src, float* y) {
+  typedef _Float16 hv_t __attribute__((ext_vector_type(DP)));
+  const hv_t v = *reinterpret_cast<const hv_t*>(src);
+#pragma unroll
+  for (int i = 0; i < DP; ++i) y[i] = (float)v[i];
+}
+
+// Rotated values y[0..DP) of elements d0 .. d0+DP-1 of one head vector `v`
+// (fp16 bits, D elements). Pairs: (i, i + D/2) for style 1, (2i, 2i+1) for
+// style 2; style 0 copies. DP is even and divides D/2, d0 is a multiple of DP.
+template <int D, int DP>
+__device__ __forceinline__ void rope_range(const uint16_t* v, int d0, int style, const float (*cs)[2], float* y) {
+  float a[DP];
+  load_halves<DP>(v + d0, a);
+  if (style == 1) {
+    const bool lo = d0 < D / 2;
+    float b[DP];
+    load_halves<DP>(v + (lo ? d0 + D / 2 : d0 - D / 2), b);
+    const int i0 = lo ? d0 : d0 - D / 2;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      const float c = cs[i0 + i][0], s = cs[i0 + i][1];
+      y[i] = lo ? a[i] * c - b[i] * s : b[i] * s + a[i] * c;
+    }
+  } else if (style == 2) {
+#pragma unroll
+    for (int i = 0; i < DP; i += 2) {
+      const int pi = (d0 + i) >> 1;
+      const float c = cs[pi][0], s = cs[pi][1];
+      y[i] = a[i] * c - a[i + 1] * s;
+      y[i + 1] = a[i] * s + a[i + 1] * c;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < DP; ++i) y[i] = a[i];
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams p) {
+  constexpr int NC = D / 32;  // 32-wide d blocks of the score product
+  constexpr int NE = D / 16;  // 16-row d tiles of the value product
+  constexpr int DP = D / 16;  // d values per thread in the merge
+  constexpr int HS = D + 4;   // floats per head in a partial slot: o[D], max, sum, pad
+  __shared__ float cs[D / 2][2];
+  __shared__ int s_last;
+
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g4 = l >> 4;
+  const int unit = blockIdx.x / p.C, chunk = blockIdx.x % p.C;
+  const int tile = unit % p.T, bk = unit / p.T;  // bk = b * Hkv + kv head
+  const int b = bk / p.Hkv, kvh = bk % p.Hkv;
+  const int L = p.lengths[b];
+  const bool valid = L >= 0 && L < p.S && L <= p.max_cached;
+  const int span = p.steps * kAttnBlock;
+  const int first = (chunk * kAttnWaves + w) * span;
+  const int kend = valid ? min(L, first + span) : 0;  // this wave's cached positions: [first, kend)
+  const int hv = min(16, p.g - 16 * tile);            // real query heads in this tile
+  const int nslots = p.C * kAttnWaves;
+
+  const uint16_t* kbase = p.kc + (int64_t)bk * p.S * D;
+  const uint16_t* vbase = p.vc + (int64_t)bk * D * p.S;
+  // Key rows: A-row r of a 32-position block at k0 is position
+  // k0 + 8(r/4) + 4blk + r%4 (blk = 0, 1); values: d row 16e + l%16,
+  // positions k0 + 8(l/16) .. +7.
+  h8 kx[2][NC];
+  h8 vx[NE];
+  auto load_block = [&](int k0) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int pos = k0 + 8 * (r16 >> 2) + 4 * blk + (r16 & 3);
+      const uint16_t* kr = kbase + (int64_t)pos * D + 8 * g4;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) kx[blk][c] = *reinterpret_cast<const h8*>(kr + 32 * c);
+    }
+#pragma unroll
+    for (int e = 0; e < NE; ++e)
+      vx[e] = *reinterpret_cast<const h8*>(vbase + (int64_t)(16 * e + r16) * p.S + k0 + 8 * g4);
+  };
+  if (first < kend) load_block(first);  // in flight while the angles are computed
+
+  if (tid < D / 2) {
+    float c = 1.f, s = 0.f;
+    if (p.style != 0 && valid) {
+      const double ang = (double)L * exp2(-(2.0 * tid / D) * p.log2_theta);
+      double sd, cd;
+      sincos(ang, &sd, &cd);
+      c = (float)cd;
+      s = (float)sd;
+    }
+    cs[tid][0] = c;
+    cs[tid][1] = s;
+  }
+  __syncthreads();
+
+  const uint16_t* row = p.qkv + (int64_t)b * p.qkv_stride;
+  if (first < kend) {
+    // Rotated queries of the tile as the B operand: lane l holds head l%16,
+    // d = 32c + 8(l/16) .. +7 of each block c.
+    h8 bq[NC];
+    {
+      const int hl = 16 * tile + r16;
+      float y[NC][8];
+      if (hl < p.g) {
+        const uint16_t* qh = row + (int64_t)(kvh * p.g + hl) * D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) rope_range<D, 8>(qh, 32 * c + 8 * g4, p.style, cs, y[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) y[c][e] = 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) bq[c][e] = (_Float16)y[c][e];
+    }
+
+    f4 acc[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
+    float m_run = kNoMax, l_run = 0.f;
+
+    for (int k0 = first; k0 < kend; k0 += kAttnBlock) {
+      // Scores: lane l gets head l%16, positions kb + 4blk + t (t = 0..3).
+      const int kb = k0 + 8 * g4;
+      float s[2][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        f4 sa = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NC; ++c) sa = __builtin_amdgcn_mfma_f32_16x16x32_f16(kx[blk][c], bq[c], sa, 0, 0, 0);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          s[blk][t] = (kb + 4 * blk + t < L) ? sa[t] * p.scale_log2 : -INFINITY;
+          mx = fmaxf(mx, s[blk][t]);
+        }
+      }
+      mx = xor_max(mx, 16);
+      mx = xor_max(mx, 32);
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      float psum = 0.f;
+      h4 pb[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const float pv = exp2f(s[blk][t] - m_new);
+          psum += pv;
+          pb[blk][t] = (_Float16)pv;
+        }
+      l_run = l_run * alpha + psum;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) acc[e] *= alpha;
+      if (k0 + kAttnBlock > L) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (kb + j >= L) vx[e][j] = (_Float16)0.f;
+      }
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          const h4 va = h4{vx[e][4 * blk], vx[e][4 * blk + 1], vx[e][4 * blk + 2], vx[e][4 * blk + 3]};
+          acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[blk], acc[e], 0, 0, 0);
+        }
+      if (k0 + kAttnBlock < kend) load_block(k0 + kAttnBlock);
+    }
+    l_run = xor_sum(l_run, 16);
+    l_run = xor_sum(l_run, 32);
+
+    // Partial state of this wave: head l%16, d = 16e + 4(l/16) .. +3.
+    if (r16 < hv) {
+      float* ph = p.part + (((int64_t)unit * nslots + chunk * kAttnWaves + w) * 16 + r16) * HS;
+#pragma unroll
+      for (int e = 0; e < NE; ++e) *reinterpret_cast<f4*>(ph + 16 * e + 4 * g4) = acc[e];
+      if (g4 == 0) {
+        ph[D] = m_run;
+        ph[D + 1] = l_run;
+      }
+    }
+  }
+
+  // Release the partials, count this workgroup; the last one merges.
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(p.counters + unit, 1u) == (unsigned)(p.C - 1);
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  const int j = tid >> 4, d0 = (tid & 15) * DP;  // tile head j, d range [d0, d0 + DP)
+  uint16_t* out = p.out + ((int64_t)b * p.Hq + kvh * p.g + 16 * tile + j) * D + d0;
+  if (!valid) {
+    if (j < hv)
+#pragma unroll
+      for (int i = 0; i < DP; ++i) out[i] = 0x7E00;  // fp16 quiet NaN
+  } else {
+    // New token: rotated q (fp32) and key (rounded to fp16, as stored).
+    const uint16_t* kh = row + (int64_t)(p.Hq + kvh) * D;
+    const uint16_t* vh = row + (int64_t)(p.Hq + p.Hkv + kvh) * D;
+    float kr[DP], qr[DP], o[DP];
+    _Float16 k16[DP];
+    rope_range<D, DP>(kh, d0, p.style, cs, kr);
+    const bool head_ok = j < hv;
+    if (head_ok) rope_range<D, DP>(row + (int64_t)(kvh * p.g + 16 * tile + j) * D, d0, p.style, cs, qr);
+    float dot = 0.f;
+#pragma unroll
+    for (int i = 0; i < DP; ++i) {
+      k16[i] = (_Float16)kr[i];
+      dot += head_ok ? qr[i] * (float)k16[i] : 0.f;
+      o[i] = (float)reinterpret_cast<const _Float16*>(vh)[d0 + i];
+    }
+    dot = xor_sum(dot, 1);
+    dot = xor_sum(dot, 2);
+    dot = xor_sum(dot, 4);
+    dot = xor_sum(dot, 8);
+    if (head_ok) {
+      float M = dot * p.scale_log2, lsum = 1.f;
+      const float* pu = p.part + (int64_t)unit * nslots * 16 * HS + j * HS;
+      for (int sl = 0; sl < nslots && sl * span < L; ++sl) {
+        const float* ph = pu + (int64_t)sl * 16 * HS;
+        const float ms = ph[D], ls = ph[D + 1];
+        const float m2 = fmaxf(M, ms);
+        const float a = exp2f(M - m2), c = exp2f(ms - m2);
+        lsum = lsum * a + ls * c;
+#pragma unroll
+        for (int i = 0; i < DP; ++i) o[i] = o[i] * a + ph[d0 + i] * c;
+        M = m2;
+      }
+      const float inv = 1.f / lsum;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) out[i] = __builtin_bit_cast(uint16_t, (_Float16)(o[i] * inv));
+    }
+    if (tile == 0 && j == 0) {
+      uint16_t* kdst = p.kc + ((int64_t)bk * p.S + L) * D + d0;
+      uint16_t* vdst = p.vc + ((int64_t)bk * D + d0) * p.S + L;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) {
+        kdst[i] = __builtin_bit_cast(uint16_t, k16[i]);
+        vdst[(int64_t)i * p.S] = vh[d0 + i];
+      }
+    }
+  }
+  if (tid == 0) p.counters[unit] = 0u;
+}
+
+}  // namespace
+
+AttnPlan attention_plan(int B, int Hq, int Hkv, int D, int max_cached, int steps) {
+  AttnPlan pl;
+  pl.g = Hq / Hkv;
+  pl.T = (pl.g + 15) / 16;
+  const int64_t units = (int64_t)B * Hkv * pl.T;
+  const int64_t spu = max_cached > 0 ? (max_cached + kAttnBlock - 1) / kAttnBlock : 1;
+  // About eight waves per CU over 256 CUs, each wave at least one 32-position step.
+  const int64_t target = 2048;
+  pl.steps = steps > 0 ? steps : (int)std::max<int64_t>(1, (units * spu + target - 1) / target);
+  pl.C = (int)((spu + (int64_t)kAttnWaves * pl.steps - 1) / ((int64_t)kAttnWaves * pl.steps));
+  pl.units = units;
+  pl.counter_bytes = (size_t)((units * 4 + 255) / 256 * 256);
+  pl.ws_bytes = pl.counter_bytes + (size_t)units * pl.C * kAttnWaves * 16 * (D + 4) * sizeof(float);
+  return pl;
+}
+
+hipError_t launch_attention(const AttnParams& p, int D, const Launch& L) {
+  const dim3 grid((unsigned)(p.C * (int64_t)(p.units)));
+  const dim3 block(kAttnWaves * 64);
+  if (D == 64) return launch_kernel(attn_decode_kernel<64>, grid, block, 0, L, p);
+  return launch_kernel(attn_decode_kernel<128>, grid, block, 0, L, p);
+}
+
+}  // namespace awq

@@ -75,6 +75,33 @@ size_t prefill_workspace_bytes(int M, int N, int splits, bool gated);
 bool prefill_fits(int K, int N);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
+// Fused decode-step attention (rotary embedding, MHA/GQA/MQA, key-value
+// cache append). Caches: keys [B, Hkv, S, D], values d-major [B, Hkv, D, S].
+struct AttnParams {
+  const uint16_t* qkv;
+  int64_t qkv_stride;
+  uint16_t* kc;
+  uint16_t* vc;
+  const int32_t* lengths;
+  uint16_t* out;
+  float* part;         // partial softmax states (workspace)
+  uint32_t* counters;  // one per unit, zero between calls (workspace)
+  int64_t units;       // B * Hkv * T
+  int Hq, Hkv, S, max_cached, g, T, C, steps, style;
+  float scale_log2;    // softmax scale * log2(e)
+  double log2_theta;
+};
+// Work split: g query heads per kv head, T tiles of 16 of them, C workgroups
+// per unit, `steps` 32-position blocks per wave (0: chosen here); workspace
+// sizes.
+struct AttnPlan {
+  int g, T, C, steps;
+  int64_t units;
+  size_t counter_bytes, ws_bytes;
+};
+AttnPlan attention_plan(int B, int Hq, int Hkv, int D, int max_cached, int steps);
+hipError_t launch_attention(const AttnParams& p, int D, const Launch& L);
+
 // Plain streaming read of `bytes` (a multiple of 16) at `buf`; the 16 bytes at
 // `sink` may receive a value derived from the data.
 hipError_t launch_stream_read(const void* buf, uint64_t bytes, void* sink, const Launch& L);
