@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
     "quantize": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_quant.hip"),
     "decode": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_decode.hip"),
     "prefill": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_prefill.hip"),
+    "attention": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_attention.hip"),
 }
 
 
@@ -413,6 +414,85 @@ def quantize_times(awq, torch, shapes, G, dev, reps=10):
     return out
 
 
+def attention_bytes(w):
+    """Algorithmic HBM bytes of one decode-step attention call: every cached
+    key and value read once (2 x 2 x D bytes per cached token and kv head),
+    the qkv rows read, the output written, the new key and value written."""
+    return (4 * w.D * w.Hkv * w.B * w.L + 2 * w.B * (w.Hq + 2 * w.Hkv) * w.D + 2 * w.B * w.Hq * w.D
+            + 4 * w.B * w.Hkv * w.D)
+
+
+def attention_copies(w):
+    """Cache copies cycled through so that the calls read cold HBM: enough to
+    span 512 MiB (twice the last-level cache), at most 1024."""
+    n = w.B * w.Hkv * w.capacity * w.D
+    return max(1, min(1024, -(-(512 << 20) // (4 * n))))
+
+
+def attention_times(awq, lib, torch, hip, workloads, dev, reps=5):
+    """awq_attention_decode on each workload, from events at the kernel's own
+    start and end, cycling over enough copies of the caches (each copy one
+    buffer) that every call reads cold HBM; beside
+    it a plain streaming read of the same number of bytes from the same
+    buffers (keys, then values in tiles of 32 positions). Returns {name: {...}}."""
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    out = {}
+    for w in workloads:
+        S = w.capacity
+        n = w.B * w.Hkv * S * w.D
+        nbytes = attention_bytes(w)
+        R = attention_copies(w)
+        bufs = [torch.randn(2 * n, device=dev, generator=gen).half() for _ in range(R)]
+        kv = [(b[:n].view(w.B, w.Hkv, S, w.D), b[n:].view(w.B, w.Hkv, S // 32, w.D, 32)) for b in bufs]
+        qkv = torch.randn((w.B, (w.Hq + 2 * w.Hkv) * w.D), device=dev, generator=gen).half()
+        lengths = torch.full((w.B,), w.L, dtype=torch.int32, device=dev)
+        y = torch.empty((w.B, w.Hq * w.D), dtype=torch.float16, device=dev)
+        desc = awq.attention_desc(w.B, w.Hq, w.Hkv, w.D, S, w.L, rope=w.rope, theta=w.theta)
+        wsb = awq.AttentionWorkspace(dev).get(awq.attention_workspace_bytes(desc))
+        sink = torch.empty(16, dtype=torch.uint8, device=dev)
+        sr_bytes = min(nbytes, 4 * n) // 16 * 16
+
+        def call(i, e0=None, e1=None):
+            k, v = kv[i % R]
+            st = lib.awq_attention_decode_timed(ctypes.byref(desc), qkv.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                                lengths.data_ptr(), y.data_ptr(), wsb.data_ptr(), wsb.numel(),
+                                                stream, e0, e1)
+            if st:
+                raise RuntimeError(f"awq_attention_decode failed: {lib.awq_status_string(st).decode()}")
+
+        for i in range(R):
+            call(i)
+        torch.cuda.synchronize()
+        evs = hip.create(2 * R * reps)
+        for i in range(R * reps):
+            call(i, evs[2 * i], evs[2 * i + 1])
+        sevs = hip.create(2 * R * reps)
+        for i in range(R * reps):
+            st = lib.awq_stream_read(bufs[i % R].data_ptr(), sr_bytes, sink.data_ptr(), stream, sevs[2 * i],
+                                     sevs[2 * i + 1])
+            if st:
+                raise RuntimeError("awq_stream_read failed")
+        torch.cuda.synchronize()
+        ts = sorted(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(R * reps))
+        ss = sorted(hip.elapsed_ms(sevs[2 * i], sevs[2 * i + 1]) for i in range(R * reps))
+        med, smed = ts[len(ts) // 2], ss[len(ss) // 2]
+        gbps = nbytes / (med / 1e3) / 1e9
+        sr_gbps = sr_bytes / (smed / 1e3) / 1e9
+        out[w.name] = {
+            "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "D": w.D, "cached": w.L, "rope": w.rope, "theta": w.theta,
+            "launches": len(ts), "cache_copies": R, "median_us": round(med * 1e3, 3),
+            "p10_us": round(ts[len(ts) // 10] * 1e3, 3), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 3),
+            "alg_bytes": nbytes, "GBps": round(gbps, 1), "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBS, 2),
+            "stream_read_GBps_same_size": round(sr_gbps, 1), "pct_of_stream_read": round(100 * gbps / sr_gbps, 1),
+            "plan": awq.attention_plan(desc),
+        }
+        del bufs, kv, wsb
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(workload, seconds):
     """The fp64 oracle on host cores, on one layer of the stack (M=1),
     repeated until about `seconds` of CPU work; weight GB/s."""
@@ -478,7 +558,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
 
     def label(seq):
         """[(kernel, key, record)] of awq dispatches -> {(path, shape): [[records of one call], ...]}"""
-        dec = [r for r in seq if "decode_" in r[0]]
+        dec = [r for r in seq if "decode_" in r[0] and "attn_" not in r[0]]
         pre = [r for r in seq if "prefill_" in r[0]]
         out = {}
         dshapes = [sh.name for sh in synth.LLAMA2_7B_DECODE.shapes]
@@ -504,6 +584,19 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
                 name = qgrid.get(int(r[2].get("Grid_Size_X") or r[2].get("Grid_Size") or -1))
                 if name:
                     out.setdefault(("quantize", name), []).append([r])
+        # attention calls: per workload, in order, attention_copies(w) warm-up
+        # calls and the same number per timed repetition
+        att = [r for r in seq if "attn_" in r[0]]
+        if att:
+            copies = [attention_copies(w) for w in synth.ATTENTION_WORKLOADS]
+            per_rep = sum(copies)
+            if len(att) % per_rep:
+                raise RuntimeError(f"{len(att)} attention dispatches do not split into the workloads' calls")
+            i = 0
+            for w, c in zip(synth.ATTENTION_WORKLOADS, copies):
+                n = c * (len(att) // per_rep)
+                out[("attention", w.name)] = [[r] for r in att[i:i + n]]
+                i += n
         return out
 
     trace = [(_short(r["Kernel_Name"]), None, r) for r in rows(trace_dir, "bench_kernel_trace.csv")
@@ -521,7 +614,11 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     dshape = {sh.name: sh for sh in synth.LLAMA2_7B_DECODE.shapes}
     pshape = {sh.name: sh for sh in synth.LLAMA2_13B_PREFILL.shapes}
 
+    awl = {w.name: w for w in synth.ATTENTION_WORKLOADS}
+
     def alg_bytes(path, shape):
+        if path == "attention":
+            return attention_bytes(awl[shape])
         if path == "quantize":
             sh = dshape[shape]
             return 2 * sh.K * sh.N + weight_set_bytes(sh.K, sh.N, 128)
@@ -535,7 +632,10 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     lines = ["# rocprofv3 summary: W4A16 linear kernels of bench.py on one MI355X", "",
              "Workloads: LLaMA-2-7B-shaped decode stack (M=1, 32 layers x QKV 4096x12288, O 4096x4096, "
              "gate+up 4096x22016, down 11008x4096) and LLaMA-2-13B-shaped prefill GEMMs (M=512 and 2048; "
-             "QKV 5120x15360, O 5120x5120, gate+up 5120x27648, down 13824x5120), group 128.", "",
+             "QKV 5120x15360, O 5120x5120, gate+up 5120x27648, down 13824x5120), group 128; the quantiser on "
+             "the decode stack's shapes; the fused decode-step attention on the workloads named in the table "
+             "(LLaMA-2-7B MHA 32x128, LLaMA-3-8B GQA 32/8x128, Falcon-7B MQA 71/1x64; B sequences with L "
+             "tokens cached).", "",
              "Commands (each run from /tmp with TMPDIR=/tmp):", ""]
     lines += [f"    {c}" for c in commands]
     lines += ["", "The table below comes from `python bench.py --summarize-profiles TRACE FETCH WRITE` on "
@@ -546,7 +646,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
               "| path | shape | kernels of one call | calls | kernel-trace us (median / min / max) | "
               "FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|---|---|---|---|"]
-    traffic = {"decode": {}, "prefill": {}, "quantize": {}}
+    traffic = {"decode": {}, "prefill": {}, "quantize": {}, "attention": {}}
     for (path, shape), calls in sorted(dur.items()):
         per_call = [sum((int(r[2]["End_Timestamp"]) - int(r[2]["Start_Timestamp"])) / 1e3 for r in c)
                     for c in calls]
@@ -566,7 +666,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     md = os.path.join(ROOT, "profiles", "decode_prefill_llama_bench.md")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    for path in ("decode", "prefill", "quantize"):
+    for path in ("decode", "prefill", "quantize", "attention"):
+        if not traffic[path]:
+            continue
         with open(os.path.join(ROOT, "profiles", f"{path}_traffic.json"), "w") as f:
             json.dump({"kernel_source_sha": source_sha(KERNEL_SOURCES[path]), "fetch_scale": ff,
                        "write_scale": fw, "shapes": traffic[path], "source": os.path.basename(md)}, f, indent=1)
@@ -601,6 +703,7 @@ def main():
     ap.add_argument("--no-gated", action="store_true", help="skip the gated-epilogue comparison")
     ap.add_argument("--no-sweep", action="store_true", help="skip the batched-decode sweep (M = 1 .. 32)")
     ap.add_argument("--no-falcon180b", action="store_true", help="skip the 92 GB Falcon-180B-shaped stack")
+    ap.add_argument("--no-attention", action="store_true", help="skip the decode-step attention kernel")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -748,6 +851,25 @@ def main():
         eprint("[bench] gated: " + ", ".join(f"{k}: fused {v['fused_us']}us vs unfused {v['unfused_us']}us"
                                               for k, v in gated.items() if isinstance(v, dict)))
 
+    # Fused decode-step attention (rotary embedding, MHA/GQA/MQA, cache append).
+    attention = None
+    if not args.no_attention:
+        at = attention_times(awq, lib, torch, hip, synth.ATTENTION_WORKLOADS, dev)
+        adom = max(at, key=lambda k: at[k]["alg_bytes"])
+        attention = {"what": "awq_attention_decode: one generation step of attention (rotary embedding of q and "
+                             "the new k, softmax attention over the fp16 cache, append of the new key and value) "
+                             "in one kernel; HBM bytes = cached keys and values read once + qkv read + output "
+                             "and new key/value written",
+                     "cases": at,
+                     "roofline": {"bound": "hbm", "achieved": at[adom]["GBps"], "peak": HBM_PEAK_GBS,
+                                  "unit": "GB/s", "frac": round(at[adom]["GBps"] / HBM_PEAK_GBS, 4),
+                                  "traffic": traffic_entry("attention", adom),
+                                  "kernel": f"attn_decode_kernel ({adom})",
+                                  "alg_bytes_per_launch": at[adom]["alg_bytes"],
+                                  "avg_launch_us": at[adom]["median_us"]}}
+        eprint("[bench] attention: " + ", ".join(f"{k} {v['median_us']}us {v['GBps']}GB/s"
+                                                 for k, v in at.items()))
+
     qt = quantize_times(awq, torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], wl.G, dev)
     qdom = max(qt, key=lambda k: qt[k]["median_us"])
     quantize = {"what": "awq_quantize: round-to-nearest group quantiser, fp16 W [K,N] (N(0, 0.02)) -> device "
@@ -847,6 +969,7 @@ def main():
         "decode_falcon180b": falcon,
         "gated": gated,
         "quantize": quantize,
+        "attention": attention,
         "prefill": prefill,
         "cpu_baseline": cpu,
     }

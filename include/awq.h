@@ -265,9 +265,11 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
  *   qkv      B rows of qkv_stride elements (>= (Hq + 2 Hkv) D, multiple of 8)
  *   k_cache  [B, Hkv, capacity, D]: key element d of position j of (b, kv
  *            head h) at ((b*Hkv + h)*capacity + j)*D + d
- *   v_cache  [B, Hkv, D, capacity] (d-major): value element d of position j
- *            at ((b*Hkv + h)*D + d)*capacity + j, so that the value product
- *            reads consecutive positions
+ *   v_cache  [B, Hkv, capacity/32, D, 32]: tiles of 32 positions, d-major
+ *            inside a tile; value element d of position j of (b, kv head h)
+ *            at (((b*Hkv + h)*(capacity/32) + j/32)*D + d)*32 + j%32, so that
+ *            the value product reads each 32-position block as one
+ *            contiguous run of D*64 bytes
  *   lengths  int32 [B]
  *   out      [B, Hq*D]
  * Sizes: D = 64 or 128; Hq a multiple of Hkv; capacity a multiple of 32 (at

@@ -131,3 +131,48 @@ def dense_weights(K: int, N: int, seed: int = 0, layer_id: int = 0, std: float =
     LLM linear layers): input of the round-to-nearest quantiser."""
     rng = _rng(seed, 3, layer_id, K, N)
     return (rng.standard_normal(size=(K, N)) * std).astype(np.float16)
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """One generation step of attention: B sequences with L tokens cached
+    each, Hq query / Hkv key-value heads of dimension D, rotary base theta."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    D: int
+    L: int
+    theta: float = 10000.0
+    rope: str = "half"
+
+    @property
+    def capacity(self) -> int:
+        """Cache slots: room for the new token, rounded up to 32."""
+        return (self.L + 1 + 31) // 32 * 32
+
+
+# Decode-step attention of the models in the TinyChat generation benchmarks
+# (LLaMA-2-7B: 32 heads of 128; LLaMA-3-8B: 32 query / 8 key-value heads,
+# rotary base 500000; Falcon-7B: 71 query heads sharing one key-value head of
+# 64), at the >500-token prompts of the LLaMA-2 figures, at long contexts and
+# batched.
+ATTENTION_WORKLOADS = (
+    AttnWorkload("llama2-7b-mha-B1-L1024", 1, 32, 32, 128, 1024),
+    AttnWorkload("llama2-7b-mha-B1-L4096", 1, 32, 32, 128, 4096),
+    AttnWorkload("llama3-8b-gqa-B1-L4096", 1, 32, 8, 128, 4096, theta=500000.0),
+    AttnWorkload("falcon-7b-mqa-B1-L2048", 1, 71, 1, 64, 2048),
+    AttnWorkload("llama2-7b-mha-B16-L2048", 16, 32, 32, 128, 2048),
+    AttnWorkload("llama3-8b-gqa-B32-L4096", 32, 32, 8, 128, 4096, theta=500000.0),
+)
+
+
+def attention_inputs(w: AttnWorkload, seed: int = 0):
+    """qkv rows [B, (Hq + 2 Hkv) D] fp16 ~ N(0, 1) and caches k, v
+    [B, Hkv, capacity, D] fp16 ~ N(0, 1) (logical layout; positions past L are
+    filled too), lengths [B] = L."""
+    rng = _rng(seed, 4, w.B, w.Hq, w.Hkv, w.D, w.L)
+    qkv = rng.standard_normal((w.B, (w.Hq + 2 * w.Hkv) * w.D)).astype(np.float16)
+    k = rng.standard_normal((w.B, w.Hkv, w.capacity, w.D)).astype(np.float16)
+    v = rng.standard_normal((w.B, w.Hkv, w.capacity, w.D)).astype(np.float16)
+    return qkv, k, v, np.full(w.B, w.L, np.int32)

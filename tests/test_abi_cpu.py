@@ -253,4 +253,5 @@ def test_attention_plans_cover_the_cache(lib, B, Hq, Hkv, D, S, maxc, steps):
     T = -(-(Hq // Hkv) // 16)
     units = B * Hkv * T
     nbytes = awq.attention_workspace_bytes(d)
-    assert nbytes >= -(-units * 4 // 256) * 256 + units * pl["workgroups_per_unit"] * 4 * 16 * (D + 4) * 4
+    # counters, then one state (16 heads x (D + 4) floats) per workgroup
+    assert nbytes >= -(-units * 4 // 256) * 256 + units * pl["workgroups_per_unit"] * 16 * (D + 4) * 4

@@ -44,18 +44,29 @@ def _dev16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.uint16)).view(torch.float16).cuda()
 
 
+def v_to_tiles(v):
+    """Logical values [B, Hkv, S, D] -> the cache layout [B, Hkv, S/32, D, 32]."""
+    B, H, S, D = v.shape
+    return np.ascontiguousarray(v.reshape(B, H, S // 32, 32, D).transpose(0, 1, 2, 4, 3))
+
+
+def v_from_tiles(t):
+    B, H, T, D, _ = t.shape
+    return np.ascontiguousarray(t.transpose(0, 1, 2, 4, 3).reshape(B, H, T * 32, D))
+
+
 def run_step(awq, qkv, kc, vc, lengths, Hq, Hkv, max_cached, rope, theta, steps=0, workspace=None, scale=0.0):
     """One call on device copies; returns (out [B, Hq, D], k cache, v cache
     in the logical [B, Hkv, S, D] layout) as numpy fp16."""
     import torch
     B, _, S, D = kc.shape
     kd = _dev16(kc)
-    vd = _dev16(vc.transpose(0, 1, 3, 2))
+    vd = _dev16(v_to_tiles(vc))
     ld = torch.from_numpy(np.asarray(lengths, np.int32)).cuda()
     out = awq.attention(_dev16(qkv), kd, vd, ld, Hq, Hkv, max_cached=max_cached, rope=rope, theta=theta,
                         scale=scale, steps=steps, workspace=workspace)
     torch.cuda.synchronize()
-    return (to_np16(out).reshape(B, Hq, D), to_np16(kd), np.ascontiguousarray(to_np16(vd).transpose(0, 1, 3, 2)))
+    return (to_np16(out).reshape(B, Hq, D), to_np16(kd), v_from_tiles(to_np16(vd)))
 
 
 def check_step(qkv, kc, vc, lengths, Hq, Hkv, rope, theta, got, what, scale=None):
@@ -163,7 +174,7 @@ def test_generation_loop_reuses_cache_and_workspace(awq):
     kc[:, :, :30] = rng.standard_normal((B, Hkv, 30, D)).astype(np.float16)
     vc[:, :, :30] = rng.standard_normal((B, Hkv, 30, D)).astype(np.float16)
     kd = _dev16(kc)
-    vd = _dev16(vc.transpose(0, 1, 3, 2))
+    vd = _dev16(v_to_tiles(vc))
     ws = awq.AttentionWorkspace(torch.device("cuda"))
     k_ref, v_ref = kc.copy(), vc.copy()
     for step in range(12):
@@ -191,8 +202,7 @@ def test_generation_loop_reuses_cache_and_workspace(awq):
 def test_errors(awq):
     import torch
     log("attention errors")
-    kd = torch.zeros((1, 2, 64, 64), dtype=torch.float16, device="cuda")
-    vd = torch.zeros((1, 2, 64, 64), dtype=torch.float16, device="cuda")
+    kd, vd = awq.kv_cache(1, 2, 64, 64, "cuda")
     qkv = torch.zeros((1, 8 * 64), dtype=torch.float16, device="cuda")
     ld = torch.zeros(1, dtype=torch.int32, device="cuda")
     with pytest.raises(awq.AWQError):  # max_cached must be below capacity
@@ -204,4 +214,18 @@ def test_errors(awq):
     k3 = torch.zeros((1, 2, 64, 96), dtype=torch.float16, device="cuda")
     with pytest.raises(awq.AWQError):  # head_dim 96 is not supported
         awq.attention(torch.zeros((1, 8 * 96), dtype=torch.float16, device="cuda"), k3,
-                      torch.zeros((1, 2, 96, 64), dtype=torch.float16, device="cuda"), ld, 4, 2)
+                      torch.zeros((1, 2, 2, 96, 32), dtype=torch.float16, device="cuda"), ld, 4, 2)
+
+
+@pytest.mark.parametrize("w", __import__("synth").ATTENTION_WORKLOADS, ids=lambda w: w.name)
+def test_bench_workloads_sampled(awq, w):
+    # The bench's workloads at full size, with the automatic work split it
+    # times; the oracle checks three sequences (first, middle, last).
+    import synth
+    log(f"attention workload {w.name}")
+    qkv, kc, vc, lengths = synth.attention_inputs(w, seed=1)
+    out, k_after, v_after = run_step(awq, qkv, kc, vc, lengths, w.Hq, w.Hkv, w.L, w.rope, w.theta)
+    bs = sorted({0, w.B // 2, w.B - 1})
+    check_step(qkv[bs], kc[bs], vc[bs], lengths[bs], w.Hq, w.Hkv, w.rope, w.theta,
+               (out[bs], k_after[bs], v_after[bs]), w.name)
+    assert np.all(np.isfinite(out.astype(np.float32)))

@@ -399,11 +399,14 @@ class AttentionWorkspace:
 
 
 def kv_cache(B: int, kv_heads: int, capacity: int, head_dim: int, device=None):
-    """Zero-filled key cache [B, Hkv, capacity, D] and d-major value cache
-    [B, Hkv, D, capacity] (fp16) in the layouts ``attention`` reads."""
+    """Zero-filled key cache [B, Hkv, capacity, D] and value cache
+    [B, Hkv, capacity/32, D, 32] (tiles of 32 positions, d-major inside a
+    tile), fp16, in the layouts ``attention`` reads."""
     torch = _torch()
+    if capacity % 32:
+        raise ValueError("capacity must be a multiple of 32")
     k = torch.zeros((B, kv_heads, capacity, head_dim), dtype=torch.float16, device=device)
-    v = torch.zeros((B, kv_heads, head_dim, capacity), dtype=torch.float16, device=device)
+    v = torch.zeros((B, kv_heads, capacity // 32, head_dim, 32), dtype=torch.float16, device=device)
     return k, v
 
 
@@ -412,21 +415,22 @@ def attention(qkv, k_cache, v_cache, lengths, q_heads: int, kv_heads: int, max_c
     """One generation step of attention with the rotary embedding fused in.
 
     qkv [B, >= (Hq + 2 Hkv) D] fp16 (rows [q heads | k heads | v heads]),
-    k_cache [B, Hkv, S, D] and v_cache [B, Hkv, D, S] fp16 (updated in place:
+    k_cache [B, Hkv, S, D] and v_cache [B, Hkv, S/32, D, 32] fp16 (see
+    ``kv_cache``; updated in place:
     slot lengths[b] receives the new rotated key and the value), lengths [B]
     int32 on the device (tokens already cached). Returns out [B, Hq * D] fp16.
     ``max_cached`` bounds lengths on the host (default S - 1)."""
     torch = _torch()
     _need(k_cache, torch.float16, "k_cache", 4)
-    _need(v_cache, torch.float16, "v_cache", 4)
+    _need(v_cache, torch.float16, "v_cache", 5)
     _need(lengths, torch.int32, "lengths", 1)
     if not isinstance(qkv, torch.Tensor) or qkv.dtype != torch.float16 or not qkv.is_cuda or qkv.dim() != 2:
         raise TypeError("qkv must be a 2-D fp16 GPU tensor")
     if qkv.stride(1) != 1:
         raise ValueError("qkv rows must be contiguous")
     B, Hkv, S, D = k_cache.shape
-    if Hkv != kv_heads or v_cache.shape != (B, Hkv, D, S):
-        raise ValueError("k_cache must be [B, Hkv, S, D] and v_cache [B, Hkv, D, S]")
+    if Hkv != kv_heads or S % 32 or v_cache.shape != (B, Hkv, S // 32, D, 32):
+        raise ValueError("k_cache must be [B, Hkv, S, D] and v_cache [B, Hkv, S/32, D, 32]")
     if qkv.shape[0] != B or lengths.shape[0] != B or qkv.shape[1] < (q_heads + 2 * kv_heads) * D:
         raise ValueError("qkv must be [B, >= (Hq + 2 Hkv) D] and lengths [B]")
     desc = attention_desc(B, q_heads, kv_heads, D, S, S - 1 if max_cached is None else int(max_cached),

@@ -12,21 +12,27 @@
 //   * Work unit = (sequence b, key/value head, tile of 16 query heads of that
 //     head's group). A workgroup of four waves takes one contiguous range of
 //     cached positions of one unit; each wave streams `steps` blocks of 32
-//     positions of its own sub-range with online softmax, and writes its
-//     partial state (running max, sum, unnormalised output) to the workspace.
+//     positions of its own sub-range with online softmax; the waves' states
+//     (running max, sum, unnormalised output) are merged through LDS and the
+//     workgroup's state goes to the workspace.
 //   * Scores on the matrix cores: v_mfma_f32_16x16x32_f16 with the keys as the
 //     A operand (lane l loads 16 bytes of key row k(l%16) at d = 8(l/16) of
 //     each 32-wide d block) and the rotated queries as B. The key rows of a
 //     32-position block are ordered so that the score tile a lane receives
 //     (head l%16, four positions) is exactly the B operand of
-//     v_mfma_f32_16x16x16_f16 for the value product, and the values it needs
-//     (eight consecutive positions of one d row) are one 16-byte load from the
-//     d-major value cache. No cross-lane moves besides two max reductions.
+//     v_mfma_f32_16x16x32_f16 for the value product once the two blocks of a
+//     32-position step are side by side, and the values it needs (eight
+//     consecutive positions of one d row) are one 16-byte load from the value
+//     cache, kept in tiles of 32 positions (d-major inside a tile) so that
+//     each load instruction reads one contiguous KiB. No cross-lane moves
+//     besides two max reductions per step.
 //   * The rotation angles are computed once per workgroup in fp64 (rate
 //     theta^(-2i/D) times the position), kept as fp32 cos/sin in LDS.
 //   * The last workgroup of a unit to finish (an agent-scope counter in the
-//     workspace, returned to zero by that workgroup) merges the partial states
-//     in a fixed order, adds the new token (its rotated key rounded to fp16,
+//     workspace, returned to zero by that workgroup) merges the states in a
+//     fixed order, all its threads loading several states at once (one
+//     round trip to memory for up to 8 x 16 / heads-per-tile workgroups),
+//     adds the new token (its rotated key rounded to fp16,
 //     as it is stored, and its value), writes the fp16 output and, for the
 //     unit's first tile, appends the key and value to the caches.
 //   * Positions at or beyond a sequence's length are masked: their scores are
@@ -48,6 +54,24 @@ namespace {
 constexpr int kAttnWaves = 4;
 constexpr int kAttnBlock = 32;    // positions per wave step
 constexpr float kNoMax = -3.0e38f;  // running max before any position
+
+// Workgroup states travel between XCDs, whose L2 caches are not coherent
+// with each other. They are written and read with agent-scope relaxed atomic
+// accesses, which the hardware performs coherently without flushing or
+// invalidating the L2 (a fence at agent scope would do both, for the whole
+// cache, in every workgroup). Ordering: every wave waits until its state
+// stores are acknowledged (s_waitcnt on all counters), then the workgroup
+// barrier, then thread 0 increments the unit's counter; the last workgroup
+// reads the states only after its own increment has returned.
+__device__ __forceinline__ void coherent_store2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__builtin_bit_cast(uint32_t, a) | ((uint64_t)__builtin_bit_cast(uint32_t, b) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_load2(const float* p, float& a, float& b) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  a = __builtin_bit_cast(float, (uint32_t)v);
+  b = __builtin_bit_cast(float, (uint32_t)(v >> 32));
+}
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
@@ -96,9 +120,10 @@ template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams p) {
   constexpr int NC = D / 32;  // 32-wide d blocks of the score product
   constexpr int NE = D / 16;  // 16-row d tiles of the value product
-  constexpr int DP = D / 16;  // d values per thread in the merge
-  constexpr int HS = D + 4;   // floats per head in a partial slot: o[D], max, sum, pad
+  constexpr int DP = D / 16;  // d values per thread when states are merged
+  constexpr int HS = D + 4;   // floats per head of a state: o[D], max, sum, pad
   __shared__ float cs[D / 2][2];
+  __shared__ float red[kAttnWaves][16][HS];  // the waves' states, then the merge groups'
   __shared__ int s_last;
 
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r16 = l & 15, g4 = l >> 4;
@@ -110,14 +135,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
   const int span = p.steps * kAttnBlock;
   const int first = (chunk * kAttnWaves + w) * span;
   const int kend = valid ? min(L, first + span) : 0;  // this wave's cached positions: [first, kend)
-  const int hv = min(16, p.g - 16 * tile);            // real query heads in this tile
-  const int nslots = p.C * kAttnWaves;
+  const bool wg_keys = valid && chunk * kAttnWaves * span < L;
+  const int hv = min(16, p.g - 16 * tile);  // real query heads in this tile
 
+  // Keys [S, D] per (b, kv head); values in tiles of 32 positions, d-major
+  // inside a tile: element (d, j) at ((j / 32) * D + d) * 32 + j % 32.
   const uint16_t* kbase = p.kc + (int64_t)bk * p.S * D;
-  const uint16_t* vbase = p.vc + (int64_t)bk * D * p.S;
-  // Key rows: A-row r of a 32-position block at k0 is position
-  // k0 + 8(r/4) + 4blk + r%4 (blk = 0, 1); values: d row 16e + l%16,
-  // positions k0 + 8(l/16) .. +7.
+  const uint16_t* vbase = p.vc + (int64_t)bk * p.S * D;
+  // A-row r of key block blk (of a 32-position step at k0) is position
+  // k0 + 8(r/4) + 4blk + r%4; lane l's values are d row 16e + l%16,
+  // positions k0 + 8(l/16) .. +7 (one contiguous 1 KiB per load instruction).
   h8 kx[2][NC];
   h8 vx[NE];
   auto load_block = [&](int k0) {
@@ -128,9 +155,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
 #pragma unroll
       for (int c = 0; c < NC; ++c) kx[blk][c] = *reinterpret_cast<const h8*>(kr + 32 * c);
     }
+    const uint16_t* vt = vbase + (int64_t)(k0 / kAttnBlock) * D * kAttnBlock + 8 * g4;
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
-      vx[e] = *reinterpret_cast<const h8*>(vbase + (int64_t)(16 * e + r16) * p.S + k0 + 8 * g4);
+    for (int e = 0; e < NE; ++e) vx[e] = *reinterpret_cast<const h8*>(vt + (16 * e + r16) * kAttnBlock);
   };
   if (first < kend) load_block(first);  // in flight while the angles are computed
 
@@ -149,6 +176,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
   __syncthreads();
 
   const uint16_t* row = p.qkv + (int64_t)b * p.qkv_stride;
+  f4 acc[NE];
+#pragma unroll
+  for (int e = 0; e < NE; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNoMax, l_run = 0.f;
   if (first < kend) {
     // Rotated queries of the tile as the B operand: lane l holds head l%16,
     // d = 32c + 8(l/16) .. +7 of each block c.
@@ -172,11 +203,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
         for (int e = 0; e < 8; ++e) bq[c][e] = (_Float16)y[c][e];
     }
 
-    f4 acc[NE];
-#pragma unroll
-    for (int e = 0; e < NE; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
-    float m_run = kNoMax, l_run = 0.f;
-
     for (int k0 = first; k0 < kend; k0 += kAttnBlock) {
       // Scores: lane l gets head l%16, positions kb + 4blk + t (t = 0..3).
       const int kb = k0 + 8 * g4;
@@ -198,15 +224,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
       const float m_new = fmaxf(m_run, mx);
       const float alpha = exp2f(m_run - m_new);
       m_run = m_new;
+      // Probabilities of positions kb .. kb+7: the B operand of the value
+      // product (head l%16, eight consecutive positions per lane).
       float psum = 0.f;
-      h4 pb[2];
+      h8 pb;
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const float pv = exp2f(s[blk][t] - m_new);
           psum += pv;
-          pb[blk][t] = (_Float16)pv;
+          pb[4 * blk + t] = (_Float16)pv;
         }
       l_run = l_run * alpha + psum;
 #pragma unroll
@@ -219,38 +247,105 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
             if (kb + j >= L) vx[e][j] = (_Float16)0.f;
       }
 #pragma unroll
-      for (int e = 0; e < NE; ++e)
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-          const h4 va = h4{vx[e][4 * blk], vx[e][4 * blk + 1], vx[e][4 * blk + 2], vx[e][4 * blk + 3]};
-          acc[e] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pb[blk], acc[e], 0, 0, 0);
-        }
+      for (int e = 0; e < NE; ++e) acc[e] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vx[e], pb, acc[e], 0, 0, 0);
       if (k0 + kAttnBlock < kend) load_block(k0 + kAttnBlock);
     }
     l_run = xor_sum(l_run, 16);
     l_run = xor_sum(l_run, 32);
-
-    // Partial state of this wave: head l%16, d = 16e + 4(l/16) .. +3.
-    if (r16 < hv) {
-      float* ph = p.part + (((int64_t)unit * nslots + chunk * kAttnWaves + w) * 16 + r16) * HS;
-#pragma unroll
-      for (int e = 0; e < NE; ++e) *reinterpret_cast<f4*>(ph + 16 * e + 4 * g4) = acc[e];
-      if (g4 == 0) {
-        ph[D] = m_run;
-        ph[D + 1] = l_run;
-      }
-    }
   }
 
-  // Release the partials, count this workgroup; the last one merges.
-  __threadfence();
+  // The four waves' states (head l%16; d = 16e + 4(l/16) .. +3) merged in
+  // LDS into the workgroup's, which goes to its slot of the workspace.
+  if (wg_keys) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) *reinterpret_cast<f4*>(&red[w][r16][16 * e + 4 * g4]) = acc[e];
+    if (g4 == 0) {
+      red[w][r16][D] = m_run;
+      red[w][r16][D + 1] = l_run;
+    }
+  }
   __syncthreads();
-  if (tid == 0) s_last = atomicAdd(p.counters + unit, 1u) == (unsigned)(p.C - 1);
+  const int j = tid >> 4, d0 = (tid & 15) * DP;  // head j, d range [d0, d0 + DP)
+  if (wg_keys && j < hv) {
+    float M = kNoMax;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) M = fmaxf(M, red[ww][j][D]);
+    float lsum = 0.f, o[DP];
+#pragma unroll
+    for (int i = 0; i < DP; ++i) o[i] = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kAttnWaves; ++ww) {
+      const float c = exp2f(red[ww][j][D] - M);
+      lsum += red[ww][j][D + 1] * c;
+#pragma unroll
+      for (int i = 0; i < DP; ++i) o[i] += red[ww][j][d0 + i] * c;
+    }
+    float* ph = p.part + ((int64_t)unit * p.C + chunk) * 16 * HS + j * HS;
+#pragma unroll
+    for (int i = 0; i < DP; i += 2) coherent_store2(ph + d0 + i, o[i], o[i + 1]);
+    if ((tid & 15) == 0) coherent_store2(ph + D, M, lsum);
+  }
+
+  // Count this workgroup once its state is stored (every wave waits for its
+  // stores to be acknowledged, then the barrier); the last one merges.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0)
+    s_last = __hip_atomic_fetch_add(p.counters + unit, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+             (unsigned)(p.C - 1);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
 
-  const int j = tid >> 4, d0 = (tid & 15) * DP;  // tile head j, d range [d0, d0 + DP)
+  // Merge: the workgroups' states of this unit are spread over SG groups of
+  // threads (thread = group sg, head jj, d range), each group folds its slots
+  // with independent loads, the groups' results meet in LDS.
+  const int hvp = hv <= 1 ? 1 : hv <= 2 ? 2 : hv <= 4 ? 4 : hv <= 8 ? 8 : 16;
+  const int SG = 16 / hvp;
+  const int jj = (tid >> 4) % hvp, sg = (tid >> 4) / hvp;
+  const int nsl = valid ? min(p.C, (L + kAttnWaves * span - 1) / (kAttnWaves * span)) : 0;
+  {
+    float M = kNoMax, lsum = 0.f, o[DP];
+#pragma unroll
+    for (int i = 0; i < DP; ++i) o[i] = 0.f;
+    if (jj < hv) {
+      const float* pu = p.part + (int64_t)unit * p.C * 16 * HS + jj * HS;
+      for (int base = sg; base < nsl; base += 8 * SG) {
+        float ms[8], ls[8], os[8][DP];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int sl = base + u * SG;
+          if (sl < nsl) {
+            const float* ph = pu + (int64_t)sl * 16 * HS;
+            coherent_load2(ph + D, ms[u], ls[u]);
+#pragma unroll
+            for (int i = 0; i < DP; i += 2) coherent_load2(ph + d0 + i, os[u][i], os[u][i + 1]);
+          } else {
+            ms[u] = kNoMax;
+            ls[u] = 0.f;
+#pragma unroll
+            for (int i = 0; i < DP; ++i) os[u][i] = 0.f;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float m2 = fmaxf(M, ms[u]);
+          const float a = exp2f(M - m2), c = exp2f(ms[u] - m2);
+          lsum = lsum * a + ls[u] * c;
+#pragma unroll
+          for (int i = 0; i < DP; ++i) o[i] = o[i] * a + os[u][i] * c;
+          M = m2;
+        }
+      }
+    }
+    __syncthreads();  // the workgroup's own state in `red` has been written out
+    float* g = &red[0][0][0] + (sg * hvp + jj) * 16 * (DP + 2) + (tid & 15) * (DP + 2);
+#pragma unroll
+    for (int i = 0; i < DP; ++i) g[i] = o[i];
+    g[DP] = M;
+    g[DP + 1] = lsum;
+  }
+  __syncthreads();
+
   uint16_t* out = p.out + ((int64_t)b * p.Hq + kvh * p.g + 16 * tile + j) * D + d0;
   if (!valid) {
     if (j < hv)
@@ -278,15 +373,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
     dot = xor_sum(dot, 8);
     if (head_ok) {
       float M = dot * p.scale_log2, lsum = 1.f;
-      const float* pu = p.part + (int64_t)unit * nslots * 16 * HS + j * HS;
-      for (int sl = 0; sl < nslots && sl * span < L; ++sl) {
-        const float* ph = pu + (int64_t)sl * 16 * HS;
-        const float ms = ph[D], ls = ph[D + 1];
-        const float m2 = fmaxf(M, ms);
-        const float a = exp2f(M - m2), c = exp2f(ms - m2);
-        lsum = lsum * a + ls * c;
+      const int hvp_j = j % hvp;
+      for (int gi = 0; gi < SG; ++gi) {
+        const float* g = &red[0][0][0] + (gi * hvp + hvp_j) * 16 * (DP + 2) + (tid & 15) * (DP + 2);
+        const float mg = g[DP];
+        const float m2 = fmaxf(M, mg);
+        const float a = exp2f(M - m2), c = exp2f(mg - m2);
+        lsum = lsum * a + g[DP + 1] * c;
 #pragma unroll
-        for (int i = 0; i < DP; ++i) o[i] = o[i] * a + ph[d0 + i] * c;
+        for (int i = 0; i < DP; ++i) o[i] = o[i] * a + g[i] * c;
         M = m2;
       }
       const float inv = 1.f / lsum;
@@ -295,15 +390,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
     }
     if (tile == 0 && j == 0) {
       uint16_t* kdst = p.kc + ((int64_t)bk * p.S + L) * D + d0;
-      uint16_t* vdst = p.vc + ((int64_t)bk * D + d0) * p.S + L;
+      uint16_t* vdst = p.vc + (int64_t)bk * p.S * D + ((int64_t)(L / kAttnBlock) * D + d0) * kAttnBlock + L % kAttnBlock;
 #pragma unroll
       for (int i = 0; i < DP; ++i) {
         kdst[i] = __builtin_bit_cast(uint16_t, k16[i]);
-        vdst[(int64_t)i * p.S] = vh[d0 + i];
+        vdst[i * kAttnBlock] = vh[d0 + i];
       }
     }
   }
-  if (tid == 0) p.counters[unit] = 0u;
+  if (tid == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace
@@ -320,7 +415,7 @@ AttnPlan attention_plan(int B, int Hq, int Hkv, int D, int max_cached, int steps
   pl.C = (int)((spu + (int64_t)kAttnWaves * pl.steps - 1) / ((int64_t)kAttnWaves * pl.steps));
   pl.units = units;
   pl.counter_bytes = (size_t)((units * 4 + 255) / 256 * 256);
-  pl.ws_bytes = pl.counter_bytes + (size_t)units * pl.C * kAttnWaves * 16 * (D + 4) * sizeof(float);
+  pl.ws_bytes = pl.counter_bytes + (size_t)units * pl.C * 16 * (D + 4) * sizeof(float);
   return pl;
 }
 

@@ -76,7 +76,8 @@ bool prefill_fits(int K, int N);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
 // Fused decode-step attention (rotary embedding, MHA/GQA/MQA, key-value
-// cache append). Caches: keys [B, Hkv, S, D], values d-major [B, Hkv, D, S].
+// cache append). Caches: keys [B, Hkv, S, D], values [B, Hkv, S/32, D, 32]
+// (tiles of 32 positions, d-major inside a tile).
 struct AttnParams {
   const uint16_t* qkv;
   int64_t qkv_stride;
