@@ -76,43 +76,51 @@ __device__ __forceinline__ void coherent_load2(const float* p, float& a, float& 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 __device__ __forceinline__ float xor_sum(float v, int m) { return v + __shfl_xor(v, m); }
 
-// DP consecutive fp16 values at `src` (aligned to their size) as fp32.
+template <int N>
+using hvec_t = _Float16 __attribute__((ext_vector_type(N)));
+
+// The inputs of a rotation of elements d0 .. d0+DP-1 of one head vector (fp16
+// bits, D elements): the elements and their partners d0 +- D/2 (the pairs of
+// style 1; styles 2 and 0 use `a` only). Loaded ahead of the angle table so
+// that the load latency overlaps other work. DP divides D/2, d0 % DP == 0.
 template <int DP>
-__device__ __forceinline__ void load_halves(const uint16_t* src, float* y) {
-  typedef _Float16 hv_t __attribute__((ext_vector_type(DP)));
-  const hv_t v = *reinterpret_cast<const hv_t*>(src);
-#pragma unroll
-  for (int i = 0; i < DP; ++i) y[i] = (float)v[i];
+struct RopeSrc {
+  hvec_t<DP> a, b;
+};
+
+template <int D, int DP>
+__device__ __forceinline__ RopeSrc<DP> rope_load(const uint16_t* v, int d0) {
+  RopeSrc<DP> s;
+  s.a = *reinterpret_cast<const hvec_t<DP>*>(v + d0);
+  s.b = *reinterpret_cast<const hvec_t<DP>*>(v + (d0 < D / 2 ? d0 + D / 2 : d0 - D / 2));
+  return s;
 }
 
-// Rotated values y[0..DP) of elements d0 .. d0+DP-1 of one head vector `v`
-// (fp16 bits, D elements). Pairs: (i, i + D/2) for style 1, (2i, 2i+1) for
-// style 2; style 0 copies. DP is even and divides D/2, d0 is a multiple of DP.
+// Rotated values y[0..DP). Pairs: (i, i + D/2) for style 1, (2i, 2i+1) for
+// style 2; style 0 copies.
 template <int D, int DP>
-__device__ __forceinline__ void rope_range(const uint16_t* v, int d0, int style, const float (*cs)[2], float* y) {
-  float a[DP];
-  load_halves<DP>(v + d0, a);
+__device__ __forceinline__ void rope_apply(const RopeSrc<DP>& s, int d0, int style, const float (*cs)[2], float* y) {
   if (style == 1) {
     const bool lo = d0 < D / 2;
-    float b[DP];
-    load_halves<DP>(v + (lo ? d0 + D / 2 : d0 - D / 2), b);
     const int i0 = lo ? d0 : d0 - D / 2;
 #pragma unroll
     for (int i = 0; i < DP; ++i) {
-      const float c = cs[i0 + i][0], s = cs[i0 + i][1];
-      y[i] = lo ? a[i] * c - b[i] * s : b[i] * s + a[i] * c;
+      const float a = (float)s.a[i], b = (float)s.b[i];
+      const float c = cs[i0 + i][0], sn = cs[i0 + i][1];
+      y[i] = lo ? a * c - b * sn : b * sn + a * c;
     }
   } else if (style == 2) {
 #pragma unroll
     for (int i = 0; i < DP; i += 2) {
       const int pi = (d0 + i) >> 1;
-      const float c = cs[pi][0], s = cs[pi][1];
-      y[i] = a[i] * c - a[i + 1] * s;
-      y[i + 1] = a[i] * s + a[i + 1] * c;
+      const float c = cs[pi][0], sn = cs[pi][1];
+      const float a = (float)s.a[i], b = (float)s.a[i + 1];
+      y[i] = a * c - b * sn;
+      y[i + 1] = a * sn + b * c;
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < DP; ++i) y[i] = a[i];
+    for (int i = 0; i < DP; ++i) y[i] = (float)s.a[i];
   }
 }
 
@@ -159,7 +167,19 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
 #pragma unroll
     for (int e = 0; e < NE; ++e) vx[e] = *reinterpret_cast<const h8*>(vt + (16 * e + r16) * kAttnBlock);
   };
-  if (first < kend) load_block(first);  // in flight while the angles are computed
+  // The first block and the raw queries are requested before the sequence
+  // length arrives (any wave starting at or below max_cached may hold keys,
+  // and its first block then lies inside the cache); unused if it holds none.
+  const bool may_hold = first <= p.max_cached;
+  if (may_hold) load_block(first);
+  const uint16_t* row = p.qkv + (int64_t)b * p.qkv_stride;
+  const int hl = 16 * tile + r16;
+  RopeSrc<8> qsrc[NC];
+  if (may_hold && hl < p.g) {
+    const uint16_t* qh = row + (int64_t)(kvh * p.g + hl) * D;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qsrc[c] = rope_load<D, 8>(qh, 32 * c + 8 * g4);
+  }
 
   if (tid < D / 2) {
     float c = 1.f, s = 0.f;
@@ -175,7 +195,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
   }
   __syncthreads();
 
-  const uint16_t* row = p.qkv + (int64_t)b * p.qkv_stride;
   f4 acc[NE];
 #pragma unroll
   for (int e = 0; e < NE; ++e) acc[e] = f4{0.f, 0.f, 0.f, 0.f};
@@ -185,12 +204,10 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
     // d = 32c + 8(l/16) .. +7 of each block c.
     h8 bq[NC];
     {
-      const int hl = 16 * tile + r16;
       float y[NC][8];
       if (hl < p.g) {
-        const uint16_t* qh = row + (int64_t)(kvh * p.g + hl) * D;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) rope_range<D, 8>(qh, 32 * c + 8 * g4, p.style, cs, y[c]);
+        for (int c = 0; c < NC; ++c) rope_apply<D, 8>(qsrc[c], 32 * c + 8 * g4, p.style, cs, y[c]);
       } else {
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -286,6 +303,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
     if ((tid & 15) == 0) coherent_store2(ph + D, M, lsum);
   }
 
+  // The new token's inputs for the merge (needed by the last workgroup only;
+  // requested here so that their latency overlaps the counter step).
+  const uint16_t* kh = row + (int64_t)(p.Hq + kvh) * D;
+  const uint16_t* vh = row + (int64_t)(p.Hq + p.Hkv + kvh) * D;
+  const bool head_ok = j < hv;
+  const RopeSrc<DP> ksrc = rope_load<D, DP>(kh, d0);
+  RopeSrc<DP> qnew;
+  if (head_ok) qnew = rope_load<D, DP>(row + (int64_t)(kvh * p.g + 16 * tile + j) * D, d0);
+  const hvec_t<DP> vnew = *reinterpret_cast<const hvec_t<DP>*>(vh + d0);
+
   // Count this workgroup once its state is stored (every wave waits for its
   // stores to be acknowledged, then the barrier); the last one merges.
   __builtin_amdgcn_s_waitcnt(0);
@@ -353,19 +380,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
       for (int i = 0; i < DP; ++i) out[i] = 0x7E00;  // fp16 quiet NaN
   } else {
     // New token: rotated q (fp32) and key (rounded to fp16, as stored).
-    const uint16_t* kh = row + (int64_t)(p.Hq + kvh) * D;
-    const uint16_t* vh = row + (int64_t)(p.Hq + p.Hkv + kvh) * D;
     float kr[DP], qr[DP], o[DP];
     _Float16 k16[DP];
-    rope_range<D, DP>(kh, d0, p.style, cs, kr);
-    const bool head_ok = j < hv;
-    if (head_ok) rope_range<D, DP>(row + (int64_t)(kvh * p.g + 16 * tile + j) * D, d0, p.style, cs, qr);
+    rope_apply<D, DP>(ksrc, d0, p.style, cs, kr);
+    if (head_ok) rope_apply<D, DP>(qnew, d0, p.style, cs, qr);
     float dot = 0.f;
 #pragma unroll
     for (int i = 0; i < DP; ++i) {
       k16[i] = (_Float16)kr[i];
       dot += head_ok ? qr[i] * (float)k16[i] : 0.f;
-      o[i] = (float)reinterpret_cast<const _Float16*>(vh)[d0 + i];
+      o[i] = (float)vnew[i];
     }
     dot = xor_sum(dot, 1);
     dot = xor_sum(dot, 2);
@@ -393,8 +417,11 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
       uint16_t* vdst = p.vc + (int64_t)bk * p.S * D + ((int64_t)(L / kAttnBlock) * D + d0) * kAttnBlock + L % kAttnBlock;
 #pragma unroll
       for (int i = 0; i < DP; ++i) {
-        kdst[i] = __builtin_bit_cast(uint16_t, k16[i]);
-        vdst[i * kAttnBlock] = vh[d0 + i];
+        // element copied to a scalar first: a bit cast applied to a vector
+        // element expression reads element 0
+        const _Float16 ki = k16[i], vi = vnew[i];
+        kdst[i] = __builtin_bit_cast(uint16_t, ki);
+        vdst[i * kAttnBlock] = __builtin_bit_cast(uint16_t, vi);
       }
     }
   }
