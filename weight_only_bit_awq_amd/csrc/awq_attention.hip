@@ -124,6 +124,8 @@ __device__ __forceinline__ void rope_apply(const RopeSrc<DP>& s, int d0, int sty
   }
 }
 
+}  // namespace
+
 template <int D>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams p) {
   constexpr int NC = D / 32;  // 32-wide d blocks of the score product
@@ -427,8 +429,6 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
   }
   if (tid == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-
-}  // namespace
 
 AttnPlan attention_plan(int B, int Hq, int Hkv, int D, int max_cached, int steps) {
   AttnPlan pl;
