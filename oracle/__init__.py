@@ -14,3 +14,5 @@ from .awq_oracle import (device_layout_doc, device_words, pack_canonical,  # noq
 from .attention_oracle import (ROPE_STYLES, rope_inv_freq64, rope_pairs, rope64,  # noqa: F401,E402
                                split_qkv, softmax64, decode_step64, decode_error_scale,
                                decode_bytes)
+from .w4a8_oracle import (FP8_MAX, fp8_e4m3_value, fp8_e4m3_encode, quantize_act_fp8,  # noqa: F401,E402
+                          linear_w4a8_64, w4a8_l1_scale)
