@@ -236,6 +236,47 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
                     void* start_event, void* stop_event);
 
 /*
+ * W4A8-FP8 form of the layer. The TensorRT-LLM news page (Falcon-180B with
+ * INT4 AWQ on one H200) has the AWQ kernels compute in FP8; the readings
+ * taken (the page prints no arithmetic):
+ *   - FP8 is OCP E4M3 (bias 7, largest finite 448, no infinities), rounding
+ *     to nearest even;
+ *   - activations are quantised per row (per token) at run time, each step
+ *     one IEEE float32 operation: amax = max_k |x[m,k]|, inv = 448 / amax,
+ *     code = E4M3(x * inv), sx[m] = amax / 448 (a zero row: codes 0, sx 0);
+ *   - y[m,n] = fp16( sx[m] * sum_g s[g,n] * sum_{k in g} x8[m,k] * (q[k,n] - z[g,n]) ),
+ *     the inner sums over one group on the FP8 matrix cores in fp32 (the
+ *     products are exact), the rest in fp32.
+ * The weights (qweight, scales, zeros) are those of awq_linear. group must
+ * be a positive multiple of 128; K % group == 0; N % 8 == 0; M * K < 2^31.
+ *
+ * awq_quantize_act_fp8: x fp16 [M, K] (K % 128 == 0) -> x8 [M, K] E4M3 codes
+ *   in the kernel's layout: within each 128-column block, the 8-column chunk
+ *   c = 4j + h (columns 8c .. 8c+7, j, h = 0..3) is stored at chunk position
+ *   4h + j; sx float32 [M]. x and x8 16-byte aligned.
+ * awq_linear_w4a8: y fp16 [M, N] from fp16 x [M, K]: the activations are
+ *   quantised into the workspace (awq_linear_w4a8_workspace_bytes bytes for
+ *   the same plan, 256-byte aligned; it also holds split-K partials), then
+ *   multiplied on workgroup tiles of 128 x 128 (plan tile 2) or 256 x 256
+ *   (tile 3) with an optional K split (split_k, at most K/128 and 16); other
+ *   plan fields must be 0; NULL or zero fields are chosen automatically.
+ *   awq_linear_w4a8_ex records events at the start of its first kernel and
+ *   the end of its last (either may be NULL); awq_linear_w4a8_plan fills in
+ *   the plan a call would use.
+ */
+int awq_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, uint8_t* x8, float* sx, void* stream);
+int awq_linear_w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
+                                    size_t* bytes);
+int awq_linear_w4a8_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
+int awq_linear_w4a8(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                    const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                    uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+int awq_linear_w4a8_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                       const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                       uint16_t* y, void* workspace, size_t workspace_bytes, const awq_plan* plan,
+                       void* stream, void* start_event, void* stop_event);
+
+/*
  * Fused decode-step attention. "TinyChat: Efficient and Lightweight Chatbot
  * with AWQ", section "Speed Benchmarks": in the generation stage every
  * operation of multi-head, grouped-query and multi-query attention (MHA / GQA

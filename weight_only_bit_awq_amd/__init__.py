@@ -96,6 +96,19 @@ _SIGS = {
                                     ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "awq_stream_read": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p,
                                        ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_quantize_act_fp8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p,
+                                            ctypes.c_void_p, ctypes.c_void_p]),
+    "awq_linear_w4a8_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                                       ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_size_t)]),
+    "awq_linear_w4a8_plan": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                            ctypes.POINTER(Plan)]),
+    "awq_linear_w4a8": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),
+    "awq_linear_w4a8_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
+                                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]),
     "awq_attention_workspace_bytes": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_size_t)]),
     "awq_attention_plan": (ctypes.c_int, [ctypes.POINTER(AttnDesc), ctypes.POINTER(ctypes.c_int32),
                                           ctypes.POINTER(ctypes.c_int32)]),
@@ -355,6 +368,65 @@ def linear_silu_mul(x, qweight, scales, zeros, N: int, group: int = 128, out=Non
     return out
 
 
+def quantize_act_fp8(x):
+    """Per-token FP8 (E4M3) quantisation of fp16 x [M, K] (K % 128 == 0):
+    returns (codes uint8 [M, K] in the kernel's layout -- within each
+    128-column block, 8-column chunk 4j + h stored at position 4h + j -- and
+    scales float32 [M])."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    M, K = x.shape
+    x8 = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    sx = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(library().awq_quantize_act_fp8(x.data_ptr(), M, K, x8.data_ptr(), sx.data_ptr(), _stream(x.device)))
+    return x8, sx
+
+
+def linear_w4a8_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
+    p = _plan(plan) or Plan()
+    _check(library().awq_linear_w4a8_plan(M, K, N, group, ctypes.byref(p)))
+    return {"path": p.path, "split_k": p.split_k, "tile": p.tile}
+
+
+def linear_w4a8_workspace_bytes(M: int, K: int, N: int, group: int = 128, plan=None) -> int:
+    out = ctypes.c_size_t()
+    p = _plan(plan)
+    _check(library().awq_linear_w4a8_workspace_bytes(M, K, N, group, ctypes.byref(p) if p else None,
+                                                     ctypes.byref(out)))
+    return int(out.value)
+
+
+def linear_w4a8(x, qweight, scales, zeros, N: int, group: int = 128, out=None, workspace=None, plan=None):
+    """W4A8-FP8 layer: y[M, N] fp16 from fp16 x (quantised per token to FP8
+    inside the call) and the layer's int4 weights; group a multiple of 128."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(qweight, torch.int32, "qweight")
+    _need(scales, torch.float16, "scales", 2)
+    _need(zeros, torch.int32, "zeros", 2)
+    M, K = x.shape
+    if scales.shape != (K // group, N) or zeros.shape != (K // group, N // 8):
+        raise ValueError("scales must be [K/G, N] and zeros [K/G, N/8]")
+    if qweight.numel() < qweight_words(K, N):
+        raise ValueError("qweight is smaller than the device layout needs")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out", 2)
+    p = _plan(plan)
+    nbytes = linear_w4a8_workspace_bytes(M, K, N, group, p)
+    ws_ptr, ws_len = None, 0
+    if nbytes:
+        if workspace is None:
+            workspace = Workspace(x.device)
+        buf = workspace.get(nbytes) if isinstance(workspace, Workspace) else workspace
+        ws_ptr, ws_len = buf.data_ptr(), buf.numel() * buf.element_size()
+    _check(library().awq_linear_w4a8_ex(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), M, K,
+                                        N, group, out.data_ptr(), ws_ptr, ws_len, ctypes.byref(p) if p else None,
+                                        _stream(x.device), None, None))
+    return out
+
+
 def attention_desc(B: int, q_heads: int, kv_heads: int, head_dim: int, capacity: int, max_cached: int,
                    qkv_stride: int = 0, rope: str = "half", theta: float = 10000.0, scale: float = 0.0,
                    steps: int = 0) -> AttnDesc:
@@ -456,7 +528,7 @@ def attention(qkv, k_cache, v_cache, lengths, q_heads: int, kv_heads: int, max_c
     return out
 
 
-__all__ = ["attention", "attention_desc", "attention_plan", "attention_workspace_bytes", "kv_cache",
+__all__ = ["quantize_act_fp8", "linear_w4a8", "linear_w4a8_plan", "linear_w4a8_workspace_bytes", "attention", "attention_desc", "attention_plan", "attention_workspace_bytes", "kv_cache",
            "AttentionWorkspace", "library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_silu_mul",
            "linear_silu_mul_plan", "linear_silu_mul_workspace_bytes", "linear_plan",
            "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",

@@ -22,7 +22,7 @@ LIB_NAME = "libawq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["awq_api.cpp", "awq_pack.hip", "awq_decode.hip", "awq_prefill.hip", "awq_probe.hip", "awq_quant.hip",
-           "awq_attention.hip"]
+           "awq_attention.hip", "awq_w4a8.hip"]
 
 ARCH = "gfx950"
 COMMON_FLAGS = [

@@ -253,6 +253,47 @@ int workspace_out(int64_t M, int64_t K, int64_t N, int group, const awq_plan* pl
 
 namespace {
 
+// W4A8-FP8: shapes the FP8 path supports (groups of whole 128-row bands).
+int w4a8_check(int64_t M, int64_t K, int64_t N, int G) {
+  int st = check_dims(M, K, N);
+  if (st) return st;
+  if (G <= 0 || G % 128) return AWQ_ERR_GROUP;
+  if (K % G || N % 8) return AWQ_ERR_SHAPE;
+  if (M * K >= ((int64_t)1 << 31) || !awq::prefill_fits((int)K, (int)N)) return AWQ_ERR_SHAPE;
+  return AWQ_OK;
+}
+
+// Tile 2 (128 x 128) or 3 (256 x 256) and the K split; explicit plan fields
+// (tile, split_k) are honoured, the rest chosen by the prefill cost model.
+int w4a8_plan(int64_t M, int64_t K, int64_t N, const awq_plan* plan, int* tile, int* splits) {
+  *tile = plan ? plan->tile : 0;
+  *splits = plan ? plan->split_k : 0;
+  if (plan && (plan->path || plan->waves || plan->tpw || plan->x_stage)) return AWQ_ERR_PLAN;
+  if (*tile == 1 || *tile < 0 || *tile > 3 || *splits < 0 || *splits > 16) return AWQ_ERR_PLAN;
+  if (*splits > (int)(K / 128)) return AWQ_ERR_PLAN;
+  awq::prefill_auto_plan((int)M, (int)K, (int)N, tile, splits);
+  return AWQ_OK;
+}
+
+int w4a8_run(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
+             int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
+             const awq_plan* plan, const awq::Launch& L) {
+  int st = w4a8_check(M, K, N, group);
+  if (st) return st;
+  if (M == 0 || N == 0) return AWQ_OK;
+  if (K == 0) return hip_status(awq::launch_fill_zero(y, M * N, L.stream));
+  if (!x || !qweight || !scales || !zeros || !y) return AWQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 4) || !aligned(zeros, 4))
+    return AWQ_ERR_ALIGN;
+  int tile, splits;
+  if ((st = w4a8_plan(M, K, N, plan, &tile, &splits))) return st;
+  const size_t need = awq::w4a8_workspace_bytes((int)M, (int)K, (int)N, splits);
+  if (!workspace || workspace_bytes < need) return AWQ_ERR_WORKSPACE;
+  if (!aligned(workspace, 256)) return AWQ_ERR_ALIGN;
+  const awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
+  return hip_status(awq::launch_w4a8(a, tile, splits, workspace, L));
+}
+
 // Attention: validation of the descriptor and the work split it implies.
 int attention_check(const awq_attn_desc* d, awq::AttnPlan* pl) {
   if (!d) return AWQ_ERR_NULL;
@@ -452,6 +493,58 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream, voi
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
                int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
   return awq_linear_ex(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+int awq_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, uint8_t* x8, float* sx, void* stream) {
+  if (M < 0 || K < 0 || M > kMaxDim || K > kMaxDim || K % 128) return AWQ_ERR_SHAPE;
+  if (M == 0 || K == 0) return AWQ_OK;
+  if (!x || !x8 || !sx) return AWQ_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x8, 16) || !aligned(sx, 4)) return AWQ_ERR_ALIGN;
+  const awq::Launch L{(hipStream_t)stream, nullptr, nullptr};
+  return hip_status(awq::launch_act_quant_fp8(x, (int)M, (int)K, x8, sx, L));
+}
+
+int awq_linear_w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
+                                    size_t* bytes) {
+  if (!bytes) return AWQ_ERR_NULL;
+  int st = w4a8_check(M, K, N, group);
+  if (st) return st;
+  if (M == 0 || K == 0 || N == 0) {
+    *bytes = 0;
+    return AWQ_OK;
+  }
+  int tile, splits;
+  if ((st = w4a8_plan(M, K, N, plan, &tile, &splits))) return st;
+  *bytes = awq::w4a8_workspace_bytes((int)M, (int)K, (int)N, splits);
+  return AWQ_OK;
+}
+
+int awq_linear_w4a8_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan) {
+  if (!plan) return AWQ_ERR_NULL;
+  int st = w4a8_check(M, K, N, group);
+  if (st) return st;
+  int tile, splits;
+  if ((st = w4a8_plan(M, K, N, plan, &tile, &splits))) return st;
+  *plan = awq_plan{};
+  plan->path = 2;
+  plan->tile = tile;
+  plan->split_k = splits;
+  return AWQ_OK;
+}
+
+int awq_linear_w4a8(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                    int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  const awq::Launch L{(hipStream_t)stream, nullptr, nullptr};
+  return w4a8_run(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, L);
+}
+
+int awq_linear_w4a8_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                       int64_t M, int64_t K, int64_t N, int group, uint16_t* y, void* workspace,
+                       size_t workspace_bytes, const awq_plan* plan, void* stream, void* start_event,
+                       void* stop_event) {
+  const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
+  return w4a8_run(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, plan, L);
 }
 
 int awq_attention_workspace_bytes(const awq_attn_desc* desc, size_t* bytes) {

@@ -36,6 +36,19 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// Copy 16 (or 4) bytes per lane from the buffer at byte offset `off` into
+// LDS at lds + 16 * lane (lds + 4 * lane); out-of-range offsets write zeros.
+// The size must be a literal here: inside a template the host pass of the
+// compiler rejects it.
+__device__ __forceinline__ void load_to_lds16(rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void load_to_lds4(rsrc_t r, char* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, off, 0, 0, 0);
+}
+
 __device__ __forceinline__ h2 as_h2(uint32_t u) { return __builtin_bit_cast(h2, u); }
 __device__ __forceinline__ uint32_t as_u32(h2 v) { return __builtin_bit_cast(uint32_t, v); }
 

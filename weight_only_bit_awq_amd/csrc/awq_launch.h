@@ -75,6 +75,17 @@ size_t prefill_workspace_bytes(int M, int N, int splits, bool gated);
 bool prefill_fits(int K, int N);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
+// Sum of `splits` fp32 partials ws[s][mn] in increasing s, rounded to fp16.
+hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int64_t mn, int splits, const Launch& L);
+
+// W4A8-FP8: per-token FP8 (E4M3) activation quantiser, and the layer on the
+// FP8 matrix cores (G a multiple of 128). The workspace holds the FP8
+// activations [M, K] (128-column blocks with permuted 8-column chunks), the
+// token scales and, with splits > 1, the fp32 partials.
+hipError_t launch_act_quant_fp8(const uint16_t* x, int M, int K, uint8_t* x8, float* sx, const Launch& L);
+size_t w4a8_workspace_bytes(int M, int K, int N, int splits);
+hipError_t launch_w4a8(const LinearArgs& a, int tile, int splits, void* ws, const Launch& L);
+
 // Fused decode-step attention (rotary embedding, MHA/GQA/MQA, key-value
 // cache append). Caches: keys [B, Hkv, S, D], values [B, Hkv, S/32, D, 32]
 // (tiles of 32 positions, d-major inside a tile).

@@ -39,7 +39,6 @@
 namespace awq {
 
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
 
 template <int WM, int WN, int MTW, int NTW, int KS, int GS>
 struct PrefillCfg {
@@ -78,16 +77,6 @@ struct WeightWords<4> {
     return __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
   }
 };
-
-// Copy 16 (or 4) bytes per lane from the buffer at byte offset `off` into
-// LDS at lds + 16 * lane (lds + 4 * lane). The size must be a literal here:
-// inside a template the host pass of the compiler rejects it.
-__device__ __forceinline__ void load_to_lds16(rsrc_t r, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, 0);
-}
-__device__ __forceinline__ void load_to_lds4(rsrc_t r, char* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 4, off, 0, 0, 0);
-}
 
 // Byte offset of 16-byte chunk `chunk` of slab row `row` (rows of CPR chunks).
 template <int CPR>
@@ -392,6 +381,11 @@ hipError_t launch_prefill_k(const LinearArgs& a, int splits, float* ws, bool gat
 }
 
 }  // namespace
+
+hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int64_t mn, int splits, const Launch& L) {
+  return launch_kernel(prefill_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, L,
+                       static_cast<const float*>(ws), y, mn, splits);
+}
 
 int prefill_steps(int K, int tile) { return (K + (tile == 1 ? 63 : 127)) / (tile == 1 ? 64 : 128); }
 
