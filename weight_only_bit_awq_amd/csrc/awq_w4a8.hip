@@ -23,12 +23,13 @@
 // 128-row band, j = 0..3, the device layout's row set of that lane) as one
 // contiguous 32-byte run.
 //
-// GEMM structure as in the fp16 prefill kernel: workgroup tiles of
-// (16 MTW WM) x (16 NTW WN) outputs, one 128-row K step per group row, the
-// activation slab copied global -> LDS by buffer loads with the LDS bit one
-// step ahead (XOR-swizzled 16-byte chunks), scales and packed zero words
-// alongside, each wave's weight words loaded into registers one step ahead,
-// decoded to FP8 right before use, and split-K through an fp32 workspace
+// GEMM: workgroup tiles of (16 MTW) x (16 NTW WN) outputs, each of the WN
+// waves over all rows of its NTW column tiles (every weight decoded once per
+// workgroup), one 128-row K step per group row; the activation slab copied
+// global -> LDS by buffer loads with the LDS bit one step ahead
+// (XOR-swizzled 16-byte chunks); each lane's weight words, zero word and
+// scale loaded into registers two steps ahead and decoded to FP8 one step
+// ahead, under the current step's MFMAs; split-K through an fp32 workspace
 // summed in a fixed order by the prefill reduction kernel.
 #include "awq_device.h"
 #include "awq_launch.h"
@@ -112,22 +113,18 @@ __global__ __launch_bounds__(256) void act_quant_fp8_kernel(const uint16_t* __re
   }
 }
 
-template <int WM, int WN, int MTW, int NTW>
+template <int WN, int MTW, int NTW>
 struct W8Cfg {
-  static constexpr int NW = WM * WN;
+  static constexpr int NW = WN;                 // waves side by side along N, each over all BM rows
   static constexpr int NTH = 64 * NW;
-  static constexpr int BM = 16 * MTW * WM;
+  static constexpr int BM = 16 * MTW;
   static constexpr int BN = 16 * NTW * WN;
   static constexpr int KS = 128;                // one step = one 128-row band
   static constexpr int CPR = KS / 16;           // 16-byte chunks per slab row (fp8)
   static constexpr int A_BYTES = BM * KS;       // one activation slab
   static constexpr int A_DMA = BM * CPR / NTH;  // 16-byte loads per thread per step
-  static constexpr int SC_OFF = A_BYTES;        // BN/2 dwords of scales
-  static constexpr int ZW_OFF = A_BYTES + NTH * 4;
-  static constexpr int STAGE = A_BYTES + 2 * NTH * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE;
+  static constexpr int LDS_BYTES = 2 * A_BYTES;
   static_assert((BM * CPR) % NTH == 0, "activation slab must split evenly over the threads");
-  static_assert(BN / 2 <= NTH && BN / 8 <= NTH, "scale and zero rows exceed one dword per thread");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 };
 
@@ -139,16 +136,31 @@ __device__ __forceinline__ uint32_t swz8(uint32_t row, uint32_t chunk) {
   return row * 128u + ((chunk ^ ((row >> 1) & 7u)) << 4);
 }
 
-template <int WM, int WN, int MTW, int NTW>
-__global__ __launch_bounds__(64 * WM * WN) void w4a8_gemm_kernel(const uint8_t* __restrict__ x8,
-                                                                 const float* __restrict__ sx,
-                                                                 const uint32_t* __restrict__ qw,
-                                                                 const uint16_t* __restrict__ scales,
-                                                                 const uint32_t* __restrict__ zeros,
-                                                                 uint16_t* __restrict__ y, float* __restrict__ ws,
-                                                                 int M, int K, int N, int G, int NT, int n_mtiles,
-                                                                 int n_tiles, int split_steps, uint32_t qw_bytes) {
-  using C = W8Cfg<WM, WN, MTW, NTW>;
+// What a lane needs of one step for its NTW column tiles: its 16-byte slice
+// of each 128-row weight tile, the packed zero word and the fp16 scale of
+// its column.
+template <int NTW>
+struct StepWords {
+  u4 w[NTW];
+  uint32_t zw[NTW];
+  uint32_t sc[NTW];
+};
+
+// Each wave owns NTW column tiles over all BM rows, so every weight word is
+// decoded once per workgroup. A step's words, zero words and scales arrive
+// in registers two steps ahead and are decoded to FP8 one step ahead, in the
+// shadow of the current step's MFMAs (the loop body has no branches: loads
+// past the last step read zero through out-of-range buffer offsets).
+template <int WN, int MTW, int NTW>
+__global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __restrict__ x8,
+                                                          const float* __restrict__ sx,
+                                                          const uint32_t* __restrict__ qw,
+                                                          const uint16_t* __restrict__ scales,
+                                                          const uint32_t* __restrict__ zeros,
+                                                          uint16_t* __restrict__ y, float* __restrict__ ws, int M,
+                                                          int K, int N, int G, int NT, int n_mtiles, int n_tiles,
+                                                          int split_steps, uint32_t qw_bytes) {
+  using C = W8Cfg<WN, MTW, NTW>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   const int u = xcd_remap(blockIdx.x, gridDim.x);
@@ -161,8 +173,7 @@ __global__ __launch_bounds__(64 * WM * WN) void w4a8_gemm_kernel(const uint8_t* 
   const int n0 = ntile * C::BN;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wv / WN, wn = wv % WN;
+  const int wn = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = lane >> 4;
   const int groups = K / G;
   const int nsteps = K / C::KS;
@@ -179,40 +190,55 @@ __global__ __launch_bounds__(64 * WM * WN) void w4a8_gemm_kernel(const uint8_t* 
   uint32_t a_goff[C::A_DMA];
 #pragma unroll
   for (int j = 0; j < C::A_DMA; ++j) {
-    const uint32_t p = (uint32_t)(j * C::NW + wv) * 64u + (uint32_t)lane;
+    const uint32_t p = (uint32_t)(j * C::NW + wn) * 64u + (uint32_t)lane;
     const uint32_t row = p / C::CPR;
     const uint32_t ch = (p % C::CPR) ^ ((row >> 1) & 7u);
     const int grow = m0 + (int)row;
     a_goff[j] = grow < M ? (uint32_t)grow * (uint32_t)K + 16u * ch : kOOB;
   }
-  // Scales: dword tid holds columns 2c, 2c+1; zeros: packed word c.
-  const int sc_col = n0 + 2 * tid;
-  const bool sc_ok = tid < C::BN / 2 && sc_col < N;
-  const int zw_w = n0 / 8 + tid;
-  const bool zw_ok = tid < C::BN / 8 && 8 * zw_w < N;
-  uint32_t b_off[NTW];
+  // This lane's column in each of its tiles.
+  uint32_t b_off[NTW], z_off[NTW], s_off[NTW], zsh[NTW];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
-    const int col = n0 + 16 * (NTW * wn + nt);
-    b_off[nt] = col < N ? (uint32_t)(col / 16) * 1024u + (uint32_t)lane * 16u : kOOB;
+    const int c0 = n0 + 16 * (NTW * wn + nt);
+    const int col = c0 + (lane & 15);
+    b_off[nt] = c0 < N ? (uint32_t)(c0 / 16) * 1024u + (uint32_t)lane * 16u : kOOB;
+    z_off[nt] = col < N ? (uint32_t)(col / 8) * 4u : kOOB;
+    s_off[nt] = col < N ? (uint32_t)col * 2u : kOOB;
+    zsh[nt] = 4u * (uint32_t)(col % 8);
   }
 
   auto issue_stage = [&](int step, int buf) {
-    char* st = smem + buf * C::STAGE;
+    char* st = smem + buf * C::A_BYTES;
+    const uint32_t bad = (uint32_t)!(step < step1) << 31;
     const uint32_t k0 = (uint32_t)step * C::KS;
 #pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j) load_to_lds16(rx, st + (j * C::NW + wv) * 1024, a_goff[j] + k0);
-    const int g = (step * C::KS) / G;
-    load_to_lds4(rs, st + C::SC_OFF + wv * 256,
-                 sc_ok ? ((uint32_t)g * (uint32_t)N + (uint32_t)sc_col) * 2u : kOOB);
-    load_to_lds4(rz, st + C::ZW_OFF + wv * 256,
-                 zw_ok ? ((uint32_t)g * (uint32_t)(N / 8) + (uint32_t)zw_w) * 4u : kOOB);
+    for (int j = 0; j < C::A_DMA; ++j) load_to_lds16(rx, st + (j * C::NW + wn) * 1024, (a_goff[j] + k0) | bad);
   };
-  auto load_b = [&](int step, u4(&rb)[NTW]) {
+  auto load_step = [&](int step, StepWords<NTW>& d) {
+    const uint32_t bad = (uint32_t)!(step < step1) << 31;
     const uint32_t band = (uint32_t)step * (uint32_t)NT * 1024u;
+    const uint32_t g = (uint32_t)((step * C::KS) / G);
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-      rb[nt] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rq, b_off[nt] + band, 0, 0));
+    for (int nt = 0; nt < NTW; ++nt) {
+      d.w[nt] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rq, (b_off[nt] + band) | bad, 0, 0));
+      d.zw[nt] = __builtin_amdgcn_raw_buffer_load_b32(rz, (z_off[nt] + g * (uint32_t)(N / 8) * 4u) | bad, 0, 0);
+      d.sc[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, (s_off[nt] + g * (uint32_t)N * 2u) | bad, 0, 0);
+    }
+  };
+  const DecodeConsts kc = decode_consts();
+  auto decode_step = [&](const StepWords<NTW>& d, v8i (&bf)[NTW], float (&sc)[NTW]) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+      const ZeroConst zc = zero_const((d.zw[nt] >> zsh[nt]) & 0xFu);
+      sc[nt] = (float)__builtin_bit_cast(_Float16, (uint16_t)d.sc[nt]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u2w dd = decode_fp8(d.w[nt][j], zc, kc);
+        bf[nt][2 * j] = (int)dd[0];
+        bf[nt][2 * j + 1] = (int)dd[1];
+      }
+    }
   };
 
   f4 acc[MTW][NTW];
@@ -221,59 +247,62 @@ __global__ __launch_bounds__(64 * WM * WN) void w4a8_gemm_kernel(const uint8_t* 
 #pragma unroll
     for (int b = 0; b < NTW; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  u4 cb[NTW], rb[NTW];
+  StepWords<NTW> dn;  // words of the next step
+  v8i bf[NTW];        // current step, decoded
+  float sc[NTW];
   issue_stage(step0, 0);
-  load_b(step0, cb);
+  {
+    StepWords<NTW> d0;
+    load_step(step0, d0);
+    load_step(step0 + 1, dn);
+    __builtin_amdgcn_s_waitcnt(0);
+    decode_step(d0, bf, sc);
+  }
 
-  const DecodeConsts kc = decode_consts();
-  const int arow0 = 16 * MTW * wm + (lane & 15);
+  const int arow0 = lane & 15;
   for (int step = step0; step < step1; ++step) {
     // Explicit wait: the barrier's own fence does not count the loads that
     // write LDS directly.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool more = step + 1 < step1;
-    if (more) {
-      load_b(step + 1, rb);
-      issue_stage(step + 1, (step + 1 - step0) & 1);
-    }
-    const char* st = smem + ((step - step0) & 1) * C::STAGE;
-    const uint16_t* sc_l = reinterpret_cast<const uint16_t*>(st + C::SC_OFF);
-    const uint32_t* zw_l = reinterpret_cast<const uint32_t*>(st + C::ZW_OFF);
-    // Weights of the wave's column tiles as FP8 B operands: lane l holds
-    // column l%16, rows 32j + 8h .. +7 at bytes 8j .. 8j+7.
-    v8i bf[NTW];
-    float sc[NTW];
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      const int c = 16 * (NTW * wn + nt) + (lane & 15);
-      const ZeroConst zc = zero_const((zw_l[c / 8] >> (4 * (c % 8))) & 0xFu);
-      sc[nt] = (float)__builtin_bit_cast(_Float16, sc_l[c]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const u2w d = decode_fp8(cb[nt][j], zc, kc);
-        bf[nt][2 * j] = (int)d[0];
-        bf[nt][2 * j + 1] = (int)d[1];
-      }
-    }
-#pragma unroll
-    for (int mt = 0; mt < MTW; ++mt) {
-      // Activations of row arow0 + 16 mt, the 32 bytes of row group h.
-      const uint32_t row = (uint32_t)(arow0 + 16 * mt);
+    issue_stage(step + 1, (step + 1 - step0) & 1);
+    StepWords<NTW> d2;
+    load_step(step + 2, d2);
+    // Next step's weights into a second set of registers (their loads were
+    // waited for at the top), free to interleave with this step's MFMAs.
+    v8i bfn[NTW];
+    float scn[NTW];
+    decode_step(dn, bfn, scn);
+    const char* st = smem + ((step - step0) & 1) * C::A_BYTES;
+    auto a_frag = [&](int mt) {
+      const uint32_t row = (uint32_t)(arow0 + 16 * mt);  // the 32 bytes of row group h
       const u4 a0 = *reinterpret_cast<const u4*>(st + swz8(row, 2u * h));
       const u4 a1 = *reinterpret_cast<const u4*>(st + swz8(row, 2u * h + 1u));
-      const v8i af = v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+      return v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
+    };
+    // Row tiles in a software pipeline: the MFMAs of row tile mt go to their
+    // own temporaries before the group-scale multiply-adds of row tile mt-1.
+    f4 tp[2][NTW];
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const f4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[nt], f4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0,
-                                                                       127, 0, 127);
-        acc[mt][nt] += sc[nt] * t;
+    for (int mt = 0; mt <= MTW; ++mt) {
+      if (mt < MTW) {
+        const v8i af = a_frag(mt);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+          tp[mt & 1][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[nt], f4{0.f, 0.f, 0.f, 0.f}, 0, 0,
+                                                                             0, 127, 0, 127);
+      }
+      if (mt > 0) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[mt - 1][nt] += sc[nt] * tp[(mt - 1) & 1][nt];
       }
     }
-    if (more) {
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) cb[nt] = rb[nt];
+    for (int nt = 0; nt < NTW; ++nt) {
+      bf[nt] = bfn[nt];
+      sc[nt] = scn[nt];
     }
+    dn = d2;
   }
 
   // Lane l, register r of tile (mt, nt): row 4(l/16) + r, column l%16.
@@ -281,7 +310,7 @@ __global__ __launch_bounds__(64 * WM * WN) void w4a8_gemm_kernel(const uint8_t* 
   for (int mt = 0; mt < MTW; ++mt)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int row = m0 + 16 * (MTW * wm + mt) + 4 * h + r;
+      const int row = m0 + 16 * mt + 4 * h + r;
       if (row >= M) continue;
       const float s_row = sx[row];
 #pragma unroll
@@ -309,10 +338,10 @@ size_t w4a8_workspace_bytes(int M, int K, int N, int splits) {
 }
 
 namespace {
-template <int WM, int WN, int MTW, int NTW>
+template <int WN, int MTW, int NTW>
 hipError_t launch_w4a8_tile(const uint8_t* x8, const float* sx, const LinearArgs& a, int splits, float* ws,
                             const Launch& L) {
-  using C = W8Cfg<WM, WN, MTW, NTW>;
+  using C = W8Cfg<WN, MTW, NTW>;
   const int n_mtiles = (a.M + C::BM - 1) / C::BM;
   const int n_ntiles = (a.N + C::BN - 1) / C::BN;
   const int n_tiles = n_mtiles * n_ntiles;
@@ -321,7 +350,7 @@ hipError_t launch_w4a8_tile(const uint8_t* x8, const float* sx, const LinearArgs
   const int used = (nsteps + split_steps - 1) / split_steps;
   const int NT = (a.N + 15) / 16;
   const uint32_t qw_bytes = (uint32_t)((size_t)NT * ((a.K + 127) / 128) * 1024);
-  auto k = w4a8_gemm_kernel<WM, WN, MTW, NTW>;
+  auto k = w4a8_gemm_kernel<WN, MTW, NTW>;
   if (C::LDS_BYTES > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        C::LDS_BYTES);
@@ -345,8 +374,8 @@ hipError_t launch_w4a8(const LinearArgs& a, int tile, int splits, void* ws, cons
   hipError_t e = launch_act_quant_fp8(a.x, a.M, a.K, x8, sx, L.start ? Launch{L.stream, L.start, nullptr} : L);
   if (e != hipSuccess) return e;
   const Launch L2{L.stream, nullptr, L.stop};
-  if (tile == 3) return launch_w4a8_tile<2, 4, 8, 4>(x8, sx, a, splits, part, L2);
-  return launch_w4a8_tile<2, 2, 4, 4>(x8, sx, a, splits, part, L2);
+  if (tile == 3) return launch_w4a8_tile<8, 16, 2>(x8, sx, a, splits, part, L2);  // 256 x 256, 8 waves of 256 x 32
+  return launch_w4a8_tile<4, 8, 2>(x8, sx, a, splits, part, L2);                   // 128 x 128, 4 waves of 128 x 32
 }
 
 }  // namespace awq
