@@ -35,11 +35,13 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP16_DENSE_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, vendor figure
+FP8_DENSE_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 MFMA, vendor figure
 KERNEL_SOURCES = {
     "quantize": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_quant.hip"),
     "decode": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_decode.hip"),
     "prefill": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_prefill.hip"),
     "attention": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_attention.hip"),
+    "w4a8": os.path.join(ROOT, "weight_only_bit_awq_amd", "csrc", "awq_w4a8.hip"),
 }
 
 
@@ -559,23 +561,37 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     def label(seq):
         """[(kernel, key, record)] of awq dispatches -> {(path, shape): [[records of one call], ...]}"""
         dec = [r for r in seq if "decode_" in r[0] and "attn_" not in r[0]]
-        pre = [r for r in seq if "prefill_" in r[0]]
         out = {}
         dshapes = [sh.name for sh in synth.LLAMA2_7B_DECODE.shapes]
         for i, r in enumerate(dec):
             out.setdefault(("decode", dshapes[i % len(dshapes)]), []).append([r])
+        # prefill and W4A8 calls in dispatch order: a W4A8 call is the
+        # activation quantiser and its GEMM; a split-K reduction belongs to
+        # the call it follows
+        calls = {"prefill": [], "w4a8": []}
+        last = None
+        for r in seq:
+            if "prefill_reduce" in r[0] and last:
+                last.append(r)
+            elif "prefill_kernel" in r[0]:
+                last = [r]
+                calls["prefill"].append(last)
+            elif "act_quant_fp8" in r[0]:
+                last = [r]
+                calls["w4a8"].append(last)
+            elif "w4a8_gemm" in r[0] and last:
+                last.append(r)
+        # Each half (M = 512, then 2048) of the prefill calls cycles through the
+        # shapes; the W4A8 calls of a half come shape by shape in equal blocks.
         pw = synth.LLAMA2_13B_PREFILL
-        calls = []
-        for r in pre:
-            if "reduce" in r[0] and calls:
-                calls[-1].append(r)
-            else:
-                calls.append([r])
-        half = len(calls) // 2
-        for i, c in enumerate(calls):
-            Mp = pw.Ms[0] if i < half else pw.Ms[1]
-            sh = pw.shapes[(i if i < half else i - half) % len(pw.shapes)]
-            out.setdefault(("prefill", f"{sh.name}@M={Mp}"), []).append(c)
+        ns = len(pw.shapes)
+        for path, cl in calls.items():
+            half = len(cl) // 2
+            for i, c in enumerate(cl):
+                Mp = pw.Ms[0] if i < half else pw.Ms[1]
+                j = i if i < half else i - half
+                sh = pw.shapes[j % ns if path == "prefill" else (j * ns) // half]
+                out.setdefault((path, f"{sh.name}@M={Mp}"), []).append(c)
         # quantiser calls on the decode stack's shapes, told apart by their
         # grid (one 256-thread workgroup per 128-row band and 128 columns)
         qgrid = {((sh.N + 127) // 128) * ((sh.K + 127) // 128) * 256: sh.name for sh in synth.LLAMA2_7B_DECODE.shapes}
@@ -627,6 +643,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
             return weight_set_bytes(sh.K, sh.N, 128) + 2 * sh.K + 2 * sh.N
         name, m = shape.split("@M=")
         sh, Mp = pshape[name], int(m)
+        if path == "w4a8":  # fp16 x read, FP8 x written and read back, token scales, y written
+            return weight_set_bytes(sh.K, sh.N, 128) + 4 * Mp * sh.K + 8 * Mp + 2 * Mp * sh.N
         return weight_set_bytes(sh.K, sh.N, 128) + 2 * Mp * sh.K + 2 * Mp * sh.N
 
     lines = ["# rocprofv3 summary: W4A16 linear, quantiser and decode-attention kernels of bench.py on one MI355X", "",
@@ -646,7 +664,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
               "| path | shape | kernels of one call | calls | kernel-trace us (median / min / max) | "
               "FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes (scaled) | algorithmic bytes | ratio |",
               "|---|---|---|---|---|---|---|---|---|---|"]
-    traffic = {"decode": {}, "prefill": {}, "quantize": {}, "attention": {}}
+    traffic = {"decode": {}, "prefill": {}, "quantize": {}, "attention": {}, "w4a8": {}}
     for (path, shape), calls in sorted(dur.items()):
         per_call = [sum((int(r[2]["End_Timestamp"]) - int(r[2]["Start_Timestamp"])) / 1e3 for r in c)
                     for c in calls]
@@ -676,7 +694,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     md = os.path.join(ROOT, "profiles", "linear_quantize_attention_llama_falcon.md")
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
-    for path in ("decode", "prefill", "quantize", "attention"):
+    for path in ("decode", "prefill", "quantize", "attention", "w4a8"):
         if not traffic[path]:
             continue
         with open(os.path.join(ROOT, "profiles", f"{path}_traffic.json"), "w") as f:
@@ -714,6 +732,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true", help="skip the batched-decode sweep (M = 1 .. 32)")
     ap.add_argument("--no-falcon180b", action="store_true", help="skip the 92 GB Falcon-180B-shaped stack")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-step attention kernel")
+    ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8-FP8 prefill comparison")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -940,6 +959,54 @@ def main():
                                "traffic": traffic_entry("prefill", big), "kernel": f"prefill_kernel ({big})"}
         eprint(f"[bench] prefill: M=2048 {prefill['M=2048']} TFLOP/s, M=512 {prefill['M=512']} TFLOP/s")
 
+    # W4A8-FP8 form of the same prefill layers: per-token FP8 activations,
+    # FP8 matrix cores; one call = the activation quantiser + the GEMM (+ the
+    # split-K reduction), timed from the first kernel's start to the last's end.
+    w4a8 = None
+    if not args.no_prefill and not args.no_w4a8:
+        pw = synth.LLAMA2_13B_PREFILL
+        w4a8 = {"what": "awq_linear_w4a8: activations quantised per token to FP8 E4M3 inside the call, int4 weights "
+                        "decoded to exact FP8 (q - z), FP8 MFMA, group and token scales in fp32; same LLaMA-2-13B "
+                        "shapes and activations as the prefill section",
+                "unit": "TFLOP/s", "shapes": {}}
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for Mp in pw.Ms:
+            play, _ = build_stack(awq, torch, pw, Mp, dev, args.seed + 1, layers=1)
+            tot_flop, tot_ms = 0.0, 0.0
+            for name, L in play:
+                nb = awq.linear_w4a8_workspace_bytes(Mp, L.K, L.N, 128)
+                wsb = torch.empty(max(nb, 256), dtype=torch.uint8, device=dev)
+                cargs = (L.x.data_ptr(), L.qw.data_ptr(), L.s.data_ptr(), L.zw.data_ptr(), Mp, L.K, L.N, 128,
+                         L.y.data_ptr(), wsb.data_ptr(), wsb.numel(), None, stream)
+                for _ in range(5):
+                    if lib.awq_linear_w4a8_ex(*cargs, None, None):
+                        raise RuntimeError("awq_linear_w4a8 failed")
+                evs = hip.create(2 * args.prefill_reps)
+                for i in range(args.prefill_reps):
+                    lib.awq_linear_w4a8_ex(*cargs, evs[2 * i], evs[2 * i + 1])
+                torch.cuda.synchronize()
+                ts = sorted(hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(args.prefill_reps))
+                med = ts[len(ts) // 2]
+                fl = 2.0 * Mp * L.K * L.N
+                tot_flop += fl
+                tot_ms += med
+                w4a8["shapes"][f"{name}@M={Mp}"] = {
+                    "K": L.K, "N": L.N, "median_us": round(med * 1e3, 2),
+                    "p10_us": round(ts[len(ts) // 10] * 1e3, 2), "p90_us": round(ts[(9 * len(ts)) // 10] * 1e3, 2),
+                    "TFLOPs": round(fl / (med / 1e3) / 1e12, 1), "plan": awq.linear_w4a8_plan(Mp, L.K, L.N, 128)}
+                del wsb
+            w4a8[f"M={Mp}"] = round(tot_flop / (tot_ms / 1e3) / 1e12, 1)
+            del play
+            torch.cuda.empty_cache()
+        big = max((k for k in w4a8["shapes"] if k.endswith("M=2048")), key=lambda k: w4a8["shapes"][k]["median_us"])
+        wv = w4a8["shapes"][big]["TFLOPs"]
+        w4a8["roofline"] = {"bound": "mfma", "achieved": wv, "peak": FP8_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                            "frac": round(wv / FP8_DENSE_PEAK_TFLOPS, 4), "traffic": traffic_entry("w4a8", big),
+                            "kernel": f"act_quant_fp8_kernel + w4a8_gemm_kernel ({big})"}
+        if prefill:
+            w4a8["speedup_over_w4a16_M2048"] = round(w4a8["M=2048"] / prefill["M=2048"], 3)
+        eprint(f"[bench] w4a8: M=2048 {w4a8['M=2048']} TFLOP/s, M=512 {w4a8['M=512']} TFLOP/s")
+
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
@@ -981,6 +1048,7 @@ def main():
         "quantize": quantize,
         "attention": attention,
         "prefill": prefill,
+        "w4a8": w4a8,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
