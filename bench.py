@@ -495,6 +495,109 @@ def attention_times(awq, lib, torch, hip, workloads, dev, reps=5):
     return out
 
 
+def decode_chain(awq, lib, torch, hip, dev, steps, warmup, n_layers=32, B=1, L=1024, seed=11):
+    """One generation step of a LLaMA-2-7B-shaped decoder (hidden 4096, 32
+    heads of 128, MLP 11008, group 128) through the library's calls, each
+    output feeding the next call: QKV projection -> fused attention (rotary
+    embedding, append to the layer's cache, L tokens cached) -> O projection
+    -> gated gate+up (silu(gate) * up) -> down projection -> next layer.
+    RMSNorm, residual adds, embedding and LM head are not part of it. The
+    step is captured in a HIP graph and replayed (per-token latency); an
+    eager pass with kernel events splits it into linears and attention."""
+    Hq = Hkv = 32
+    D, Hd, F, G = 128, 4096, 11008, 128
+    S = (L + 1 + 31) // 32 * 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    ws = awq.Workspace(dev)
+    xs = [torch.randn((B, Hd), device=dev, generator=gen).half() for _ in range(2)]
+    qkv = torch.empty((B, (Hq + 2 * Hkv) * D), dtype=torch.float16, device=dev)
+    att = torch.empty((B, Hq * D), dtype=torch.float16, device=dev)
+    oo = torch.empty((B, Hd), dtype=torch.float16, device=dev)
+    hh = torch.empty((B, F), dtype=torch.float16, device=dev)
+    lengths = torch.full((B,), L, dtype=torch.int32, device=dev)
+    desc = awq.attention_desc(B, Hq, Hkv, D, S, L, rope="half", theta=10000.0)
+    aws = awq.AttentionWorkspace(dev).get(awq.attention_workspace_bytes(desc))
+    gu_bytes = awq.linear_silu_mul_workspace_bytes(B, Hd, 2 * F, G)
+    gws = torch.empty(max(gu_bytes, 256), dtype=torch.uint8, device=dev)
+    layers = []
+    for li in range(n_layers):
+        x_in, x_out = xs[li % 2], xs[(li + 1) % 2]
+        lq = Layer(awq, torch, Hd, (Hq + 2 * Hkv) * D, G, gen, x_in, qkv, ws, dev)
+        lo = Layer(awq, torch, Hd, Hd, G, gen, att, oo, ws, dev)
+        lg = Layer(awq, torch, Hd, 2 * F, G, gen, oo, hh, ws, dev)
+        ld = Layer(awq, torch, F, Hd, G, gen, hh, x_out, ws, dev)
+        kc, vc = awq.kv_cache(B, Hkv, S, D, dev)
+        kc.normal_(generator=gen)
+        vc.normal_(generator=gen)
+        layers.append((lq, lo, lg, ld, kc, vc))
+    gargs = lambda lg: (lg.x.data_ptr(), lg.qw.data_ptr(), lg.s.data_ptr(), lg.zw.data_ptr(), B, Hd, 2 * F, G,
+                        hh.data_ptr(), gws.data_ptr(), gws.numel(), None)
+
+    def run(events=None):
+        i = 0
+        for lq, lo, lg, ld, kc, vc in layers:
+            calls = [("linear", lq), ("attention", (kc, vc)), ("linear", lo), ("gated", lg), ("linear", ld)]
+            for kind, obj in calls:
+                e0, e1 = (events[2 * i], events[2 * i + 1]) if events else (None, None)
+                if kind == "linear":
+                    st = lib.awq_linear_timed(*obj.args, None, stream, e0, e1)
+                elif kind == "gated":
+                    st = lib.awq_linear_silu_mul_ex(*gargs(obj), stream, e0, e1)
+                else:
+                    st = lib.awq_attention_decode_timed(ctypes.byref(desc), qkv.data_ptr(), obj[0].data_ptr(),
+                                                        obj[1].data_ptr(), lengths.data_ptr(), att.data_ptr(),
+                                                        aws.data_ptr(), aws.numel(), stream, e0, e1)
+                if st:
+                    raise RuntimeError(f"chain call failed: {lib.awq_status_string(st).decode()}")
+                i += 1
+        return i
+
+    n_calls = run()
+    torch.cuda.synchronize()
+    evs = hip.create(2 * n_calls)
+    run(evs)
+    torch.cuda.synchronize()
+    kinds = (["linear", "attention", "linear", "linear", "linear"] * n_layers)
+    split = {"linear": 0.0, "attention": 0.0}
+    for i, k in enumerate(kinds):
+        split[k] += hip.elapsed_ms(evs[2 * i], evs[2 * i + 1])
+    # graph of one step, replayed
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stream = ctypes.c_void_p(side.cuda_stream)
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        run()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    wbytes = n_layers * sum(weight_set_bytes(K, N, G) for K, N in ((Hd, (Hq + 2 * Hkv) * D), (Hd, Hd), (Hd, 2 * F),
+                                                                   (F, Hd)))
+    kvbytes = n_layers * 4 * D * Hkv * B * L
+    del g, layers
+    torch.cuda.empty_cache()
+    return {"workload": f"llama2-7b-shaped decoder step: {n_layers} layers x (QKV, attention, O, gated gate+up, "
+                        f"down), B={B}, {L} tokens cached, G={G}",
+            "excluded": "RMSNorm, residual adds, embedding, LM head",
+            "ms_per_token": round(ms, 4), "tokens_per_s": round(1e3 / ms * B, 1),
+            "eager_linear_ms": round(split["linear"], 4), "eager_attention_ms": round(split["attention"], 4),
+            "weight_bytes": wbytes, "kv_bytes": kvbytes,
+            "GBps": round((wbytes + kvbytes) / (ms / 1e3) / 1e9, 1)}
+
+
 def cpu_baseline(workload, seconds):
     """The fp64 oracle on host cores, on one layer of the stack (M=1),
     repeated until about `seconds` of CPU work; weight GB/s."""
@@ -733,6 +836,7 @@ def main():
     ap.add_argument("--no-falcon180b", action="store_true", help="skip the 92 GB Falcon-180B-shaped stack")
     ap.add_argument("--no-attention", action="store_true", help="skip the decode-step attention kernel")
     ap.add_argument("--no-w4a8", action="store_true", help="skip the W4A8-FP8 prefill comparison")
+    ap.add_argument("--no-chain", action="store_true", help="skip the decoder-step chain (linears + attention)")
     ap.add_argument("--kernel-reps", type=int, default=3, help="eager passes with per-kernel events")
     ap.add_argument("--prefill-reps", type=int, default=50)
     ap.add_argument("--summarize-profiles", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -899,6 +1003,12 @@ def main():
         eprint("[bench] attention: " + ", ".join(f"{k} {v['median_us']}us {v['GBps']}GB/s"
                                                  for k, v in at.items()))
 
+    chain = None
+    if not args.no_chain:
+        chain = decode_chain(awq, lib, torch, hip, dev, max(5, args.steps // 2), 3)
+        eprint(f"[bench] decoder step chain: {chain['ms_per_token']} ms/token ({chain['tokens_per_s']} tokens/s), "
+               f"eager split linear {chain['eager_linear_ms']} ms / attention {chain['eager_attention_ms']} ms")
+
     qt = quantize_times(awq, torch, [(sh.name, sh.K, sh.N) for sh in wl.shapes], wl.G, dev)
     qdom = max(qt, key=lambda k: qt[k]["median_us"])
     quantize = {"what": "awq_quantize: round-to-nearest group quantiser, fp16 W [K,N] (N(0, 0.02)) -> device "
@@ -1047,6 +1157,7 @@ def main():
         "gated": gated,
         "quantize": quantize,
         "attention": attention,
+        "decode_layer_chain": chain,
         "prefill": prefill,
         "w4a8": w4a8,
         "cpu_baseline": cpu,
