@@ -600,34 +600,45 @@ def decode_chain(awq, lib, torch, hip, dev, steps, warmup, n_layers=32, B=1, L=1
 
 def cpu_baseline(workload, seconds):
     """The fp64 oracle on host cores, on one layer of the stack (M=1),
-    repeated until about `seconds` of CPU work; weight GB/s."""
+    repeated until about `seconds` of CPU work; weight GB/s. Run with the
+    BLAS library's default threads, then again on one thread for a third of
+    the time."""
     import numpy as np
 
     import oracle
     import synth
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     except Exception:
+        threadpool_limits = None
         threads = 1
     data = []
     for si, sh in enumerate(workload.shapes):
         q, z, s = synth.layer(sh.K, sh.N, workload.G, seed=0, layer_id=si, lo=workload.lo, hi=workload.hi)
         x = synth.activations(1, sh.K, seed=0, stream=si)
         data.append((x, q, z, s))
-    total_bytes = 0
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        for (x, q, z, s), sh in zip(data, workload.shapes):
-            oracle.linear64(x, q, z, s, workload.G)
-            total_bytes += weight_set_bytes(sh.K, sh.N, workload.G)
-        passes += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
+
+    def run(budget):
+        total_bytes, passes = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            for (x, q, z, s), sh in zip(data, workload.shapes):
+                oracle.linear64(x, q, z, s, workload.G)
+                total_bytes += weight_set_bytes(sh.K, sh.N, workload.G)
+            passes += 1
+            if time.perf_counter() - t0 >= budget:
+                return total_bytes / (time.perf_counter() - t0) / 1e9, passes, time.perf_counter() - t0
+
+    gbps, passes, dt = run(seconds)
+    single = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1, user_api="blas"):
+            g1, p1, d1 = run(seconds / 3)
+        single = {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                  "sample": f"{p1} pass(es) of the same layer on one BLAS thread, {d1:.1f} s"}
     return {
-        "value": round(total_bytes / dt / 1e9, 4),
+        "value": round(gbps, 4),
         "unit": "GB/s",
         "cores": int(threads),
         "kind": "oracle",
@@ -635,6 +646,7 @@ def cpu_baseline(workload, seconds):
                    f"{sum(weight_set_bytes(s.K, s.N, workload.G) for s in workload.shapes) / 1e6:.1f} MB of "
                    f"weights), numpy fp64 dequantise + BLAS matmul, {dt:.1f} s; BLAS threads={threads}, "
                    f"elementwise steps single-threaded"),
+        "single_core": single,
     }
 
 

@@ -134,3 +134,26 @@ def test_w4a8_errors(awq):
         awq.linear_w4a8(xx, qw, sd, zw, 16, 128, plan={"tile": 1})
     with pytest.raises(awq.AWQError):  # more splits than 128-row steps
         awq.linear_w4a8(xx, qw, sd, zw, 16, 128, plan={"split_k": 3})
+
+
+@pytest.mark.parametrize("si", range(4))
+def test_w4a8_prefill_workload_sampled(awq, si):
+    # The LLaMA-2-13B prefill shapes at M = 2048 (1% outlier input channels),
+    # with the automatic plan the bench times; the oracle checks sampled
+    # rows and columns.
+    w = synth.LLAMA2_13B_PREFILL
+    sh = w.shapes[si]
+    M, K, N, G = 2048, sh.K, sh.N, w.G
+    log(f"w4a8 workload {sh.name} M={M} K={K} N={N} plan={awq.linear_w4a8_plan(M, K, N, G)}")
+    q, z, s = synth.layer(K, N, G, seed=0, layer_id=si)
+    x = synth.activations(M, K, seed=0, stream=si, outlier_frac=w.outlier_frac)
+    qw, zw, sd = upload_layer(q, z, s)
+    y = to_np16(awq.linear_w4a8(x_dev(x), qw, sd, zw, N, G))
+    rng = np.random.default_rng(si)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 30, replace=False)]))
+    cols = np.unique(np.concatenate([[0, N - 1], rng.choice(N, 126, replace=False)]))
+    codes, sx = oracle.quantize_act_fp8(x[rows])
+    y64 = oracle.linear_w4a8_64(codes, sx, q[:, cols], z[:, cols], s[:, cols], G)
+    D = oracle.w4a8_l1_scale(codes, sx, q[:, cols], z[:, cols], s[:, cols], G)
+    err = float(np.max(np.abs(y[np.ix_(rows, cols)].astype(np.float64) - y64) / D))
+    assert err <= TOL, f"{sh.name}: normalised error {err:.3e}"
