@@ -247,8 +247,10 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
  *   - y[m,n] = fp16( sx[m] * sum_g s[g,n] * sum_{k in g} x8[m,k] * (q[k,n] - z[g,n]) ),
  *     the inner sums over one group on the FP8 matrix cores in fp32 (the
  *     products are exact), the rest in fp32.
- * The weights (qweight, scales, zeros) are those of awq_linear. group must
- * be a positive multiple of 128; K % group == 0; N % 8 == 0; M * K < 2^31.
+ * The weights (qweight, scales, zeros) are those of awq_linear. group is
+ * 32, 64 or a positive multiple of 128 (groups below 128 rows use one
+ * 16x16x32 FP8 MFMA per 32-row block); K % group == 0, K % 128 == 0;
+ * N % 8 == 0; M * K < 2^31.
  *
  * awq_quantize_act_fp8: x fp16 [M, K] (K % 128 == 0) -> x8 [M, K] E4M3 codes
  *   in the kernel's layout: within each 128-column block, the 8-column chunk

@@ -6,7 +6,8 @@
   inputs;
 * awq_linear_w4a8: within 2e-3 of the oracle's fp64 value of the layer on
   the quantised activations, normalised by sum_k |x8 sx| |w|, on ragged
-  shapes for both tiles and several K splits; exactly zero for q == z."""
+  shapes for both tiles, several K splits and groups of 32, 64, 128 and
+  256; exactly zero for q == z."""
 import numpy as np
 import pytest
 
@@ -68,6 +69,10 @@ SHAPES = [
     (64, 768, 72, 256, {"tile": 2}), (300, 1024, 520, 128, {"tile": 3}), (513, 640, 264, 128, {"tile": 3}),
     (130, 2048, 40, 128, {"tile": 2, "split_k": 3}), (260, 4096, 136, 256, {"tile": 3, "split_k": 5}),
     (96, 1280, 24, 128, {"tile": 3, "split_k": 2}), (2048, 1024, 256, 128, None),
+    # groups of 64 and 32 (16x16x32 FP8 MFMA per 32-row block)
+    (130, 1024, 264, 64, None), (300, 640, 136, 64, {"tile": 3}), (64, 768, 72, 64, {"tile": 2, "split_k": 2}),
+    (96, 512, 40, 32, None), (257, 1024, 264, 32, {"tile": 3}), (130, 1280, 24, 32, {"tile": 2, "split_k": 3}),
+    (512, 4608, 512, 64, None),
 ]
 
 
@@ -123,11 +128,11 @@ def test_w4a8_close_to_w4a16(awq):
 def test_w4a8_errors(awq):
     import torch
     log("w4a8 errors")
-    q, z, s = synth.layer(256, 16, 64)
+    q, z, s = synth.layer(320, 16, 64)
     qw, zw, sd = upload_layer(q, z, s)
+    with pytest.raises(awq.AWQError):  # K must be whole 128-row steps
+        awq.linear_w4a8(torch.zeros((4, 320), dtype=torch.float16, device="cuda"), qw, sd, zw, 16, 64)
     xx = torch.zeros((4, 256), dtype=torch.float16, device="cuda")
-    with pytest.raises(awq.AWQError):  # groups of 64 are not supported on this path
-        awq.linear_w4a8(xx, qw, sd, zw, 16, 64)
     q, z, s = synth.layer(256, 16, 128)
     qw, zw, sd = upload_layer(q, z, s)
     with pytest.raises(awq.AWQError):  # tile 1 does not exist here

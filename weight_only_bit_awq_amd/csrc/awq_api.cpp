@@ -257,8 +257,8 @@ namespace {
 int w4a8_check(int64_t M, int64_t K, int64_t N, int G) {
   int st = check_dims(M, K, N);
   if (st) return st;
-  if (G <= 0 || G % 128) return AWQ_ERR_GROUP;
-  if (K % G || N % 8) return AWQ_ERR_SHAPE;
+  if (!(G == 32 || G == 64 || (G > 0 && G % 128 == 0))) return AWQ_ERR_GROUP;
+  if (K % G || K % 128 || N % 8) return AWQ_ERR_SHAPE;
   if (M * K >= ((int64_t)1 << 31) || !awq::prefill_fits((int)K, (int)N)) return AWQ_ERR_SHAPE;
   return AWQ_OK;
 }

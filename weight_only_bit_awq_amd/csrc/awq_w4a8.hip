@@ -139,11 +139,11 @@ __device__ __forceinline__ uint32_t swz8(uint32_t row, uint32_t chunk) {
 // What a lane needs of one step for its NTW column tiles: its 16-byte slice
 // of each 128-row weight tile, the packed zero word and the fp16 scale of
 // its column.
-template <int NTW>
+template <int NTW, int GPS>
 struct StepWords {
   u4 w[NTW];
-  uint32_t zw[NTW];
-  uint32_t sc[NTW];
+  uint32_t zw[NTW][GPS];
+  uint32_t sc[NTW][GPS];
 };
 
 // Each wave owns NTW column tiles over all BM rows, so every weight word is
@@ -151,7 +151,11 @@ struct StepWords {
 // in registers two steps ahead and are decoded to FP8 one step ahead, in the
 // shadow of the current step's MFMAs (the loop body has no branches: loads
 // past the last step read zero through out-of-range buffer offsets).
-template <int WN, int MTW, int NTW>
+// GPS: groups per 128-row step (1 for G a multiple of 128; 2 for G = 64 and
+// 4 for G = 32, where each 32-row block of a lane's words -- one word, eight
+// FP8 bytes -- is the B operand of one v_mfma_f32_16x16x32_fp8_fp8 and the
+// group's scale multiplies the sum of its blocks).
+template <int WN, int MTW, int NTW, int GPS>
 __global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __restrict__ x8,
                                                           const float* __restrict__ sx,
                                                           const uint32_t* __restrict__ qw,
@@ -215,25 +219,29 @@ __global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __res
 #pragma unroll
     for (int j = 0; j < C::A_DMA; ++j) load_to_lds16(rx, st + (j * C::NW + wn) * 1024, (a_goff[j] + k0) | bad);
   };
-  auto load_step = [&](int step, StepWords<NTW>& d) {
+  auto load_step = [&](int step, StepWords<NTW, GPS>& d) {
     const uint32_t bad = (uint32_t)!(step < step1) << 31;
     const uint32_t band = (uint32_t)step * (uint32_t)NT * 1024u;
-    const uint32_t g = (uint32_t)((step * C::KS) / G);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       d.w[nt] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rq, (b_off[nt] + band) | bad, 0, 0));
-      d.zw[nt] = __builtin_amdgcn_raw_buffer_load_b32(rz, (z_off[nt] + g * (uint32_t)(N / 8) * 4u) | bad, 0, 0);
-      d.sc[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, (s_off[nt] + g * (uint32_t)N * 2u) | bad, 0, 0);
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) {
+        const uint32_t g = (uint32_t)((step * C::KS) / G + gi);
+        d.zw[nt][gi] = __builtin_amdgcn_raw_buffer_load_b32(rz, (z_off[nt] + g * (uint32_t)(N / 8) * 4u) | bad, 0, 0);
+        d.sc[nt][gi] = __builtin_amdgcn_raw_buffer_load_b16(rs, (s_off[nt] + g * (uint32_t)N * 2u) | bad, 0, 0);
+      }
     }
   };
   const DecodeConsts kc = decode_consts();
-  auto decode_step = [&](const StepWords<NTW>& d, v8i (&bf)[NTW], float (&sc)[NTW]) {
+  auto decode_step = [&](const StepWords<NTW, GPS>& d, v8i (&bf)[NTW], float (&sc)[NTW][GPS]) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      const ZeroConst zc = zero_const((d.zw[nt] >> zsh[nt]) & 0xFu);
-      sc[nt] = (float)__builtin_bit_cast(_Float16, (uint16_t)d.sc[nt]);
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) sc[nt][gi] = (float)__builtin_bit_cast(_Float16, (uint16_t)d.sc[nt][gi]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        const ZeroConst zc = zero_const((d.zw[nt][j * GPS / 4] >> zsh[nt]) & 0xFu);
         const u2w dd = decode_fp8(d.w[nt][j], zc, kc);
         bf[nt][2 * j] = (int)dd[0];
         bf[nt][2 * j + 1] = (int)dd[1];
@@ -247,12 +255,12 @@ __global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __res
 #pragma unroll
     for (int b = 0; b < NTW; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  StepWords<NTW> dn;  // words of the next step
-  v8i bf[NTW];        // current step, decoded
-  float sc[NTW];
+  StepWords<NTW, GPS> dn;  // words of the next step
+  v8i bf[NTW];             // current step, decoded
+  float sc[NTW][GPS];
   issue_stage(step0, 0);
   {
-    StepWords<NTW> d0;
+    StepWords<NTW, GPS> d0;
     load_step(step0, d0);
     load_step(step0 + 1, dn);
     __builtin_amdgcn_s_waitcnt(0);
@@ -266,12 +274,12 @@ __global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __res
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     issue_stage(step + 1, (step + 1 - step0) & 1);
-    StepWords<NTW> d2;
+    StepWords<NTW, GPS> d2;
     load_step(step + 2, d2);
     // Next step's weights into a second set of registers (their loads were
     // waited for at the top), free to interleave with this step's MFMAs.
     v8i bfn[NTW];
-    float scn[NTW];
+    float scn[NTW][GPS];
     decode_step(dn, bfn, scn);
     const char* st = smem + ((step - step0) & 1) * C::A_BYTES;
     auto a_frag = [&](int mt) {
@@ -280,27 +288,58 @@ __global__ __launch_bounds__(64 * WN) void w4a8_gemm_kernel(const uint8_t* __res
       const u4 a1 = *reinterpret_cast<const u4*>(st + swz8(row, 2u * h + 1u));
       return v8i{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], (int)a1[2], (int)a1[3]};
     };
-    // Row tiles in a software pipeline: the MFMAs of row tile mt go to their
-    // own temporaries before the group-scale multiply-adds of row tile mt-1.
-    f4 tp[2][NTW];
+    if constexpr (GPS == 1) {
+      // Row tiles in a software pipeline: the MFMAs of row tile mt go to
+      // their own temporaries before the group-scale multiply-adds of row
+      // tile mt-1.
+      f4 tp[2][NTW];
 #pragma unroll
-    for (int mt = 0; mt <= MTW; ++mt) {
-      if (mt < MTW) {
+      for (int mt = 0; mt <= MTW; ++mt) {
+        if (mt < MTW) {
+          const v8i af = a_frag(mt);
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            tp[mt & 1][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[nt], f4{0.f, 0.f, 0.f, 0.f}, 0,
+                                                                               0, 0, 127, 0, 127);
+        }
+        if (mt > 0) {
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt) acc[mt - 1][nt] += sc[nt][0] * tp[(mt - 1) & 1][nt];
+        }
+      }
+    } else {
+      // Each 32-row block j: the lane's bytes 8j .. 8j+7 of A and B; the
+      // blocks of one group summed by the MFMA, then scaled.
+      constexpr int BPG = 4 / GPS;  // 32-row blocks per group
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
         const v8i af = a_frag(mt);
+        f4 tg[NTW][GPS];
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
-          tp[mt & 1][nt] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[nt], f4{0.f, 0.f, 0.f, 0.f}, 0, 0,
-                                                                             0, 127, 0, 127);
-      }
-      if (mt > 0) {
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[mt - 1][nt] += sc[nt] * tp[(mt - 1) & 1][nt];
+          for (int gi = 0; gi < GPS; ++gi) {
+            f4 tt = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int jb = 0; jb < BPG; ++jb) {
+              const int j = gi * BPG + jb;
+              const long a8 = (long)(uint32_t)af[2 * j] | ((long)(uint32_t)af[2 * j + 1] << 32);
+              const long b8 = (long)(uint32_t)bf[nt][2 * j] | ((long)(uint32_t)bf[nt][2 * j + 1] << 32);
+              tt = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(a8, b8, tt, 0, 0, 0);
+            }
+            tg[nt][gi] = tt;
+          }
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+          for (int gi = 0; gi < GPS; ++gi) acc[mt][nt] += sc[nt][gi] * tg[nt][gi];
       }
     }
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       bf[nt] = bfn[nt];
-      sc[nt] = scn[nt];
+#pragma unroll
+      for (int gi = 0; gi < GPS; ++gi) sc[nt][gi] = scn[nt][gi];
     }
     dn = d2;
   }
@@ -338,7 +377,7 @@ size_t w4a8_workspace_bytes(int M, int K, int N, int splits) {
 }
 
 namespace {
-template <int WN, int MTW, int NTW>
+template <int WN, int MTW, int NTW, int GPS>
 hipError_t launch_w4a8_tile(const uint8_t* x8, const float* sx, const LinearArgs& a, int splits, float* ws,
                             const Launch& L) {
   using C = W8Cfg<WN, MTW, NTW>;
@@ -350,7 +389,7 @@ hipError_t launch_w4a8_tile(const uint8_t* x8, const float* sx, const LinearArgs
   const int used = (nsteps + split_steps - 1) / split_steps;
   const int NT = (a.N + 15) / 16;
   const uint32_t qw_bytes = (uint32_t)((size_t)NT * ((a.K + 127) / 128) * 1024);
-  auto k = w4a8_gemm_kernel<WN, MTW, NTW>;
+  auto k = w4a8_gemm_kernel<WN, MTW, NTW, GPS>;
   if (C::LDS_BYTES > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
                                        C::LDS_BYTES);
@@ -374,8 +413,17 @@ hipError_t launch_w4a8(const LinearArgs& a, int tile, int splits, void* ws, cons
   hipError_t e = launch_act_quant_fp8(a.x, a.M, a.K, x8, sx, L.start ? Launch{L.stream, L.start, nullptr} : L);
   if (e != hipSuccess) return e;
   const Launch L2{L.stream, nullptr, L.stop};
-  if (tile == 3) return launch_w4a8_tile<8, 16, 2>(x8, sx, a, splits, part, L2);  // 256 x 256, 8 waves of 256 x 32
-  return launch_w4a8_tile<4, 8, 2>(x8, sx, a, splits, part, L2);                   // 128 x 128, 4 waves of 128 x 32
+  // 256 x 256 (8 waves of 256 x 32) or 128 x 128 (4 waves of 128 x 32); groups per 128-row step
+  if (a.G % 128 == 0)
+    return tile == 3 ? launch_w4a8_tile<8, 16, 2, 1>(x8, sx, a, splits, part, L2)
+                     : launch_w4a8_tile<4, 8, 2, 1>(x8, sx, a, splits, part, L2);
+  if (a.G == 64)
+    return tile == 3 ? launch_w4a8_tile<8, 16, 2, 2>(x8, sx, a, splits, part, L2)
+                     : launch_w4a8_tile<4, 8, 2, 2>(x8, sx, a, splits, part, L2);
+  if (a.G == 32)
+    return tile == 3 ? launch_w4a8_tile<8, 16, 2, 4>(x8, sx, a, splits, part, L2)
+                     : launch_w4a8_tile<4, 8, 2, 4>(x8, sx, a, splits, part, L2);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace awq
