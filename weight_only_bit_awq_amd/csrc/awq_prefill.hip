@@ -396,7 +396,7 @@ namespace {
 // `slots` (resident workgroups per chip), each round takes one workgroup's
 // K range, and the split-K partials cost a write and a read of fp32 per
 // output per split. Times in microseconds.
-double prefill_cost(int M, int K, int N, int tile, int splits) {
+double prefill_cost(int M, int K, int N, int tile, int splits, double step_scale) {
   const int bm = tile == 3 ? 256 : 128, bn = tile == 3 ? 256 : 128;
   const double tiles = (double)((M + bm - 1) / bm) * (double)((N + bn - 1) / bn);
   const int steps = prefill_steps(K, tile);
@@ -410,17 +410,17 @@ double prefill_cost(int M, int K, int N, int tile, int splits) {
     slots = 768, t_step = 1.9;
   }
   const double rounds = std::ceil(wgs / slots);
-  const double per_wg = std::ceil((double)steps / splits) * t_step;
+  const double per_wg = std::ceil((double)steps / splits) * t_step * step_scale;
   const double reduce = splits > 1 ? 1.4e-6 * splits * (double)M * (double)N : 0.0;
   return rounds * per_wg + reduce;
 }
 
-int best_split(int M, int K, int N, int tile, double* cost) {
+int best_split(int M, int K, int N, int tile, double step_scale, double* cost) {
   const int steps = prefill_steps(K, tile);
   int best = 1;
-  double bc = prefill_cost(M, K, N, tile, 1);
+  double bc = prefill_cost(M, K, N, tile, 1, step_scale);
   for (int s = 2; s <= 8 && s * 4 <= steps; ++s) {
-    const double c = prefill_cost(M, K, N, tile, s);
+    const double c = prefill_cost(M, K, N, tile, s, step_scale);
     if (c < bc) bc = c, best = s;
   }
   if (cost) *cost = bc;
@@ -429,18 +429,18 @@ int best_split(int M, int K, int N, int tile, double* cost) {
 
 }  // namespace
 
-void prefill_auto_plan(int M, int K, int N, int* tile, int* splits) {
+void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, double step_scale) {
   // A fixed tile gets its best split; a fixed split its best tile; else both.
   if (*tile && !*splits) {
-    *splits = best_split(M, K, N, *tile, nullptr);
+    *splits = best_split(M, K, N, *tile, step_scale, nullptr);
     return;
   }
   double bc = 0;
   int bt = 0, bs = 1;
   for (int t = 2; t <= 3; ++t) {
     double c;
-    int s = *splits ? *splits : best_split(M, K, N, t, &c);
-    if (*splits) c = prefill_cost(M, K, N, t, s);
+    int s = *splits ? *splits : best_split(M, K, N, t, step_scale, &c);
+    if (*splits) c = prefill_cost(M, K, N, t, s, step_scale);
     if (!bt || c < bc) bc = c, bt = t, bs = s;
   }
   if (!*tile) *tile = bt;
