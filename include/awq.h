@@ -60,7 +60,7 @@ enum awq_status {
   AWQ_ERR_NULL = -1,      /* a required pointer is NULL                        */
   AWQ_ERR_SHAPE = -2,     /* negative size, N % 8 != 0, K % group != 0, ...   */
   AWQ_ERR_GROUP = -3,     /* group not 32, 64 or a positive multiple of 128   */
-  AWQ_ERR_ALIGN = -4,     /* a pointer is not 16-byte aligned                 */
+  AWQ_ERR_ALIGN = -4,     /* a pointer is not aligned as its entry requires    */
   AWQ_ERR_WORKSPACE = -5, /* workspace NULL or smaller than required          */
   AWQ_ERR_HIP = -6,       /* the HIP runtime reported an error (see below)    */
   AWQ_ERR_PLAN = -7,      /* an explicit plan field is out of range           */
