@@ -400,7 +400,9 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
     if (head_ok) {
       float M = dot * p.scale_log2, lsum = 1.f;
       const int hvp_j = j % hvp;
-      for (int gi = 0; gi < SG; ++gi) {
+      // group gi holds slots gi, gi + SG, ...: only the first nsl groups hold any
+      const int SGu = min(SG, nsl);
+      for (int gi = 0; gi < SGu; ++gi) {
         const float* g = &red[0][0][0] + (gi * hvp + hvp_j) * 16 * (DP + 2) + (tid & 15) * (DP + 2);
         const float mg = g[DP];
         const float m2 = fmaxf(M, mg);
