@@ -329,14 +329,17 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
   // threads (thread = group sg, head jj, d range), each group folds its slots
   // with independent loads, the groups' results meet in LDS.
   const int hvp = hv <= 1 ? 1 : hv <= 2 ? 2 : hv <= 4 ? 4 : hv <= 8 ? 8 : 16;
-  const int SG = 16 / hvp;
   const int jj = (tid >> 4) % hvp, sg = (tid >> 4) / hvp;
   const int nsl = valid ? min(p.C, (L + kAttnWaves * span - 1) / (kAttnWaves * span)) : 0;
+  // Groups in use: about four slots each (a slot folded inside a thread is a
+  // few arithmetic steps; a group folded at the end adds an LDS round trip
+  // to the chain), at most 16 / hvp.
+  const int SG = max(1, min(16 / hvp, (nsl + 3) / 4));
   {
     float M = kNoMax, lsum = 0.f, o[DP];
 #pragma unroll
     for (int i = 0; i < DP; ++i) o[i] = 0.f;
-    if (jj < hv) {
+    if (jj < hv && sg < SG) {
       const float* pu = p.part + (int64_t)unit * p.C * 16 * HS + jj * HS;
       for (int base = sg; base < nsl; base += 8 * SG) {
         float ms[8], ls[8], os[8][DP];
