@@ -1,6 +1,7 @@
-"""Seeded random shapes and plans through awq_linear and awq_linear_silu_mul:
-every plan the library accepts must meet the tolerance (any plan it rejects
-must be rejected before a launch, with AWQ_ERR_PLAN)."""
+"""Seeded random shapes and plans through awq_linear, awq_linear_silu_mul,
+awq_linear_w4a8 and awq_attention_decode: every plan the library accepts must
+meet the tolerance (any plan it rejects must be rejected before a launch,
+with AWQ_ERR_PLAN)."""
 import numpy as np
 import pytest
 
@@ -59,3 +60,56 @@ def test_random_shapes_and_plans(awq, seed):
     else:
         y = to_np16(awq.linear(x_dev(x), qw, sd, zw, N, G, plan=plan))
         check_close(y, oracle.linear64(x, q, z, s, G), oracle.l1_scale(x, q, z, s, G), what=f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_w4a8(awq, seed):
+    rng = np.random.default_rng(2000 + seed)
+    G = int(rng.choice([32, 64, 128, 256]))
+    step = max(G, 128)  # K % 128 == 0 and K % G == 0
+    K = step * int(rng.integers(1, max(2, 2048 // step) + 1))
+    N = 8 * int(rng.integers(1, 80))
+    M = int(rng.choice([1, 2, 7, 16, 33, 64, 130, 257, 513]))
+    plan = None if rng.random() < 0.4 else {"tile": int(rng.choice([2, 3])),
+                                            "split_k": int(rng.choice([0, 1, 2, 3, 5]))}
+    try:
+        used = awq.linear_w4a8_plan(M, K, N, G, plan)
+    except awq.AWQError as e:
+        assert e.status == -7, e
+        log(f"random w4a8 seed={seed} M={M} K={K} N={N} G={G} plan={plan}: rejected")
+        return
+    log(f"random w4a8 seed={seed} M={M} K={K} N={N} G={G} plan={plan} -> {used}")
+    q, z, s = synth.layer(K, N, G, seed=seed)
+    x = synth.activations(M, K, seed=seed, outlier_frac=0.01)
+    qw, zw, sd = upload_layer(q, z, s)
+    y = to_np16(awq.linear_w4a8(x_dev(x), qw, sd, zw, N, G, plan=plan)).astype(np.float64)
+    codes, sx = oracle.quantize_act_fp8(x)
+    y64 = oracle.linear_w4a8_64(codes, sx, q, z, s, G)
+    D = oracle.w4a8_l1_scale(codes, sx, q, z, s, G)
+    assert np.all(np.isfinite(y))
+    assert np.all(y[D == 0] == 0)
+    err = float(np.max(np.abs(y - y64) / np.where(D > 0, D, 1.0)))
+    assert err <= TOL, f"normalised error {err:.3e}"
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_attention(awq, seed):
+    from tests.test_gpu_attention import _inputs, check_step, run_step
+    rng = np.random.default_rng(3000 + seed)
+    D = int(rng.choice([64, 128]))
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 2, 4, 7, 16, 20]))
+    Hq = Hkv * g
+    B = int(rng.integers(1, 5))
+    S = 32 * int(rng.integers(1, 40))
+    max_cached = int(rng.integers(0, S))
+    lengths = rng.integers(0, max_cached + 1, B).astype(np.int32)
+    rope = str(rng.choice(["none", "half", "interleaved"]))
+    theta = float(rng.choice([10000.0, 500000.0]))
+    steps = int(rng.choice([0, 0, 1, 2, 3]))
+    log(f"random attention seed={seed} B={B} Hq={Hq} Hkv={Hkv} D={D} S={S} max_cached={max_cached} "
+        f"lengths={lengths.tolist()} rope={rope} steps={steps}")
+    qkv, kc, vc = _inputs(B, Hq, Hkv, D, S, 4000 + seed)
+    got = run_step(awq, qkv, kc, vc, lengths, Hq, Hkv, max_cached, rope, theta, steps=steps)
+    check_step(qkv, kc, vc, lengths, Hq, Hkv, rope, theta, got, what=f"seed {seed}")
+
