@@ -215,12 +215,6 @@ def linear64(x: np.ndarray, q: np.ndarray, z: np.ndarray, s: np.ndarray,
     return x64 @ dequant64(q, z, s, G)
 
 
-def linear64_w16(x, q, z, s, G) -> np.ndarray:
-    """Diagnostic: float64(x) @ float64(fp16-rounded W)."""
-    x64 = np.asarray(x, dtype=np.float16).astype(np.float64)
-    return x64 @ dequant16(q, z, s, G).astype(np.float64)
-
-
 def l1_scale(x, q, z, s, G) -> np.ndarray:
     """D[m, n] = sum_k |x[m, k]| * |w64[k, n]|: the L1 norm of the products
     that make up output (m, n); the error of any summation order is bounded

@@ -176,3 +176,22 @@ def attention_inputs(w: AttnWorkload, seed: int = 0):
     k = rng.standard_normal((w.B, w.Hkv, w.capacity, w.D)).astype(np.float16)
     v = rng.standard_normal((w.B, w.Hkv, w.capacity, w.D)).astype(np.float16)
     return qkv, k, v, np.full(w.B, w.L, np.int32)
+
+
+def attention_exact_inputs(w: AttnWorkload, L: int, seed: int = 0):
+    """Inputs of an attention step whose result is exact in binary arithmetic:
+    the query part of every qkv row is 0 (every score is 0), and every value
+    (cached, and the new token's) is an odd integer drawn from {-3, -1, 1, 3}
+    independently per sequence, kv head, position and element; keys ~ N(0, 1).
+    With L + 1 a power of two the output is a sum of small integers divided by
+    a power of two. Returns (qkv, k, v, lengths) like ``attention_inputs``,
+    with lengths[b] = L and capacity = L + 1 rounded up to 32."""
+    cap = (L + 1 + 31) // 32 * 32
+    rng = _rng(seed, 5, w.B, w.Hq, w.Hkv, w.D, L)
+    odd = np.array([-3.0, -1.0, 1.0, 3.0], np.float16)
+    qkv = rng.standard_normal((w.B, (w.Hq + 2 * w.Hkv) * w.D)).astype(np.float16)
+    qkv[:, :w.Hq * w.D] = 0
+    qkv[:, (w.Hq + w.Hkv) * w.D:] = odd[rng.integers(0, 4, size=(w.B, w.Hkv * w.D))]
+    k = rng.standard_normal((w.B, w.Hkv, cap, w.D)).astype(np.float16)
+    v = odd[rng.integers(0, 4, size=(w.B, w.Hkv, cap, w.D))]
+    return qkv, k, v, np.full(w.B, L, np.int32)

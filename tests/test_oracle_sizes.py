@@ -25,8 +25,13 @@ def test_mistral_sizes_scale_with_bits():
 
 def test_bf16_estimates():
     g = load()
+    # the parameter counts are the ones the page names (70B, 400B), not
+    # values derived from the sizes they are checked against
     for key in ("llama3_70b_bf16", "llama3_400b_bf16"):
-        assert oracle.model_bytes(g[key]["params_B"] * 1e9, 16) / 1e9 == pytest.approx(g[key]["GB"], rel=1e-3)
+        est = oracle.model_bytes(g[key]["params_B"] * 1e9, 16) / 1e9
+        assert est == pytest.approx(g[key]["GB"], rel=g[key]["rel_tol"])
+    # and a rule with the wrong bits per weight misses the 70B figure
+    assert oracle.model_bytes(70e9, 8) / 1e9 != pytest.approx(141.2, rel=0.01)
 
 
 def test_codes_are_half_a_byte_and_group_overhead():
