@@ -67,7 +67,8 @@ enum awq_status {
   AWQ_ERR_ARG = -8        /* a scalar argument is out of range                */
 };
 
-/* Human-readable name of a status code (static string, never NULL). */
+/* Human-readable name of a status code (static string, never NULL). Error
+ * reporting of this library; the pages define no API. */
 const char* awq_status_string(int status);
 
 /* hipError_t of the most recent AWQ_ERR_HIP on the calling thread (0 if none). */
@@ -76,7 +77,9 @@ int awq_last_hip_error(void);
 /* ABI version: bumped when a signature or a layout changes. */
 int awq_abi_version(void);
 
-/* Number of uint32 words of the device qweight layout for a [K, N] matrix. */
+/* Number of uint32 words of the device qweight layout for a [K, N] matrix
+ * (the "real" INT4 weights of TinyChat README "Usage" step 3, in the layout
+ * above); 0 if K or N is not positive. */
 size_t awq_qweight_words(int64_t K, int64_t N);
 
 /*
@@ -87,16 +90,31 @@ size_t awq_qweight_words(int64_t K, int64_t N);
  */
 int awq_pack(const uint8_t* q, int64_t K, int64_t N, uint32_t* qweight, void* stream);
 
-/* awq_unpack: inverse of awq_pack; writes q uint8 [K, N] with values 0..15. */
+/*
+ * awq_unpack: inverse of awq_pack (TinyChat README "Usage" step 3, the "real"
+ * INT4 weights read back): qweight in the device layout -> q uint8 [K, N]
+ * with values 0..15, written entirely. K % 8 == 0, N % 8 == 0; qweight
+ * 16-byte aligned. A test and interchange aid, not on the layer's path.
+ */
 int awq_unpack(const uint32_t* qweight, int64_t K, int64_t N, uint8_t* q, void* stream);
 
-/* awq_pack_zeros: zero points z uint8 [groups, N] -> packed uint32 [groups, N/8]. */
+/*
+ * awq_pack_zeros: the 4-bit zero points of the group-wise weights (TinyChat
+ * README "Usage" step 3: one per group of --q_group_size input channels and
+ * output column), z uint8 [groups, N] (low nibble used) -> packed uint32
+ * [groups, N/8], least-significant nibble first along N. N % 8 == 0; zeros
+ * 4-byte aligned.
+ */
 int awq_pack_zeros(const uint8_t* z, int64_t groups, int64_t N, uint32_t* zeros, void* stream);
 
 /*
  * awq_dequant: device qweight + scales + packed zeros -> W fp16 [K, N], with
  * W[k,n] = round_to_nearest_even_fp16((q[k,n] - z[k/G,n]) * s[k/G,n])
  * (the exact product rounded once; IEEE special values, subnormals kept).
+ * The 16-bit weights a W4A16 layer multiplies (TinyChat README "Usage" step
+ * 4, --precision W4A16), materialised: a reference and test aid, the layer
+ * itself never writes them. qweight 16-byte, scales and w 2-byte, zeros
+ * 4-byte aligned.
  */
 int awq_dequant(const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
                 int64_t K, int64_t N, int group, uint16_t* w, void* stream);
@@ -159,25 +177,36 @@ int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
 /*
  * Workspace bytes awq_linear needs for this shape and plan: 0, or
  * split_k * M * N * 4 bytes of fp32 partial sums for a prefill plan with
- * split_k > 1. The workspace needs no initialisation (every byte used is
- * written before it is read); it must be 16-byte aligned, and calls that
- * overlap in time must not share it.
+ * split_k > 1 (the split-K of the layer, reduced in a fixed order; TinyChat
+ * README "Usage" step 4, the W4A16 layer). The workspace needs no
+ * initialisation (every byte used is written before it is read); it must be
+ * 16-byte aligned, and calls that overlap in time must not share it.
+ * The _bytes forms return a status and write *bytes; awq_linear_workspace_size
+ * returns the size for the automatic plan directly, or SIZE_MAX when the
+ * arguments are invalid (awq_linear rejects them too).
  */
 int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes);
 int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group,
                                   const awq_plan* plan, size_t* bytes);
+size_t awq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int group);
 
 /*
  * awq_linear: y[M,N] (fp16) = x[M,K] (fp16) . W[K,N], W dequantised from
  * qweight/scales/zeros as in awq_dequant, accumulated in fp32, rounded once
  * to fp16 (round to nearest even). Result within 2e-3 of the exact value
  * relative to sum_k |x[m,k] * W[k,n]|; the summation order is not specified.
+ * The W4A16 layer of TinyChat README "Usage" step 4 (--precision W4A16), the
+ * generation-stage kernel of its "Speed Benchmarks". x and qweight 16-byte,
+ * zeros 4-byte, scales 2-byte aligned; y 2-byte aligned, or 8-byte aligned
+ * when the plan is a prefill plan with split_k > 1 (its reduction stores four
+ * outputs at a time). The workspace as awq_linear_workspace_bytes gives it.
  */
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
                uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
 
-/* awq_linear with an explicit plan (for tuning and for testing both paths). */
+/* awq_linear with an explicit plan (for tuning and for testing both paths);
+ * same operation, citation and rules as awq_linear. */
 int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                   const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
                   uint16_t* y, void* workspace, size_t workspace_bytes,
@@ -220,20 +249,11 @@ int awq_linear_silu_mul_ex(const uint16_t* x, const uint32_t* qweight, const uin
                            const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
                            uint16_t* y, void* workspace, size_t workspace_bytes,
                            const awq_plan* plan, void* stream, void* start_event, void* stop_event);
+/* Plan and workspace of awq_linear_silu_mul (as awq_linear_plan and
+ * awq_linear_workspace_bytes_ex). */
 int awq_linear_silu_mul_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
 int awq_linear_silu_mul_workspace_bytes(int64_t M, int64_t K, int64_t N, int group,
                                         const awq_plan* plan, size_t* bytes);
-
-/*
- * Measurement aid, not part of the layer: a plain streaming read of `bytes`
- * bytes (a multiple of 16) at device address `buf` (16-byte aligned) with
- * 16-byte loads, the achievable HBM read rate at that size against which a
- * weight-streaming launch of the same size is compared. The 16 bytes at
- * device address `sink` may receive a value derived from the data (it keeps
- * the loads live). Events as in awq_linear_timed (either may be NULL).
- */
-int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
-                    void* start_event, void* stop_event);
 
 /*
  * W4A8-FP8 form of the layer. The TensorRT-LLM news page (Falcon-180B with
@@ -266,6 +286,8 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream,
  *   the end of its last (either may be NULL); awq_linear_w4a8_plan fills in
  *   the plan a call would use.
  */
+/* The activation quantiser of the W4A8-FP8 form (TensorRT-LLM news page: AWQ
+ * kernels computing in FP8), as described above. */
 int awq_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, uint8_t* x8, float* sx, void* stream);
 int awq_linear_w4a8_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, const awq_plan* plan,
                                     size_t* bytes);
@@ -321,10 +343,13 @@ int awq_linear_w4a8_ex(const uint16_t* x, const uint32_t* qweight, const uint16_
  * lengths[b] is negative, above max_cached or not below capacity is skipped
  * on the device: its output row is set to NaN and the caches keep their
  * contents (the call still returns AWQ_OK).
- * Workspace: awq_attention_workspace_bytes() bytes. The caller zero-fills it
- * once when it is allocated; every call leaves it zero-filled again (it holds
- * per-unit completion counters, which return to zero, and partial softmax
- * states). Calls that share a workspace must not overlap (one stream).
+ * Workspace: awq_attention_workspace_bytes() bytes, 256-byte aligned. The
+ * caller zero-fills it once when it is allocated; every call leaves every
+ * byte it used zero again (it holds per-unit completion counters, which
+ * return to zero, and partial softmax states, which the merging workgroup
+ * clears after reading them), so a buffer filled once serves later calls of
+ * any shape that fits in it. Calls that share a workspace must not overlap
+ * (one stream).
  * steps: 32-position blocks per wave (0: automatic); it sets how the cached
  * positions are split over workgroups and changes only the summation order.
  * B = 0 is a valid empty call.
@@ -345,11 +370,16 @@ typedef struct awq_attn_desc {
   float softmax_scale;   /* 0: 1/sqrt(D)                                        */
 } awq_attn_desc;
 
+/* Workspace bytes of awq_attention_decode for `desc` (the counters and states
+ * described above; 0 for B = 0). */
 int awq_attention_workspace_bytes(const awq_attn_desc* desc, size_t* bytes);
 /* The work split a call with `desc` uses: workgroups per unit (a unit is a
  * sequence, kv head and tile of 16 query heads) and 32-position blocks per
  * wave. Either pointer may be NULL. */
 int awq_attention_plan(const awq_attn_desc* desc, int32_t* workgroups_per_unit, int32_t* steps);
+/* One generation step of attention (TinyChat README "Speed Benchmarks": fused
+ * MHA/GQA/MQA with the positional embedding, pre-allocated key-value cache),
+ * as described above. */
 int awq_attention_decode(const awq_attn_desc* desc, const uint16_t* qkv, uint16_t* k_cache,
                          uint16_t* v_cache, const int32_t* lengths, uint16_t* out,
                          void* workspace, size_t workspace_bytes, void* stream);

@@ -9,6 +9,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "awq.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -20,18 +22,45 @@ def lib():
     return awq.library()
 
 
-def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text)
-    return sorted(set(names))
+def declared_functions(headers=None):
+    names = set()
+    for h in headers or HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names.update(re.findall(r"\b(awq_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_header_declares_the_boundary():
-    names = declared_functions()
+    names = declared_functions([HEADER])
     for required in ("awq_pack", "awq_dequant", "awq_linear", "awq_unpack", "awq_pack_zeros",
-                     "awq_linear_workspace_bytes", "awq_qweight_words", "awq_status_string"):
+                     "awq_linear_workspace_size", "awq_linear_workspace_bytes", "awq_qweight_words",
+                     "awq_status_string"):
         assert required in names
+    # the measurement aid has a header of its own
+    assert "awq_stream_read" not in names
+    assert "awq_stream_read" in declared_functions()
+
+
+def test_every_declaration_cites_or_refers(lib):
+    # each function of the layer's header is preceded by its own comment
+    text = open(HEADER).read()
+    body = text[text.index('extern "C" {'):]
+    for name in declared_functions([HEADER]):
+        pos = re.search(r"\b" + name + r"\s*\(", re.sub(r"/\*.*?\*/", lambda m: " " * len(m.group(0)), body,
+                                                         flags=re.S)).start()
+        before = body[:pos]
+        assert "*/" in before[-1200:], f"{name}: no comment before its declaration"
+
+
+def test_workspace_size(lib):
+    import weight_only_bit_awq_amd as awq
+    size_max = ctypes.c_size_t(-1).value
+    for M, K, N in [(1, 4096, 4096), (512, 5120, 5120), (2048, 5120, 15360), (512, 13824, 5120)]:
+        assert lib.awq_linear_workspace_size(M, K, N, 128) == awq.linear_workspace_bytes(M, K, N, 128)
+    assert lib.awq_linear_workspace_size(512, 5120, 5120, 128) > 0
+    assert lib.awq_linear_workspace_size(1, 4000, 16, 128) == size_max   # K % group
+    assert lib.awq_linear_workspace_size(1, 480, 16, 96) == size_max     # group
+    assert lib.awq_linear_workspace_size(0, 4096, 4096, 128) == 0
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -110,6 +139,12 @@ def test_validation_errors_before_launch(lib):
     p.path, p.split_k = 2, 4
     assert lib.awq_linear_ex(fake, fake, fake, fake, 512, 5120, 5120, 128, fake, None, 0, ctypes.byref(p), None) == -5
     assert lib.awq_linear_ex(fake, fake, fake, fake, 512, 5120, 5120, 128, fake, fake, 16, ctypes.byref(p), None) == -5
+    # its reduction stores four outputs at a time: y must be 8-byte aligned
+    y2 = ctypes.c_void_p(0x1002)
+    big = 4 * 512 * 5120 * 4
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 512, 5120, 5120, 128, y2, fake, big, ctypes.byref(p), None) == -4
+    assert lib.awq_linear_silu_mul_ex(fake, fake, fake, fake, 2048, 5120, 27648, 128, y2, fake, 1 << 40, None, None,
+                                      None, None) == -4
 
 
 def test_plans(lib):

@@ -67,6 +67,7 @@ _SIGS = {
                                        ctypes.POINTER(Plan)]),
     "awq_linear_workspace_bytes": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                                   ctypes.POINTER(ctypes.c_size_t)]),
+    "awq_linear_workspace_size": (ctypes.c_size_t, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int]),
     "awq_linear_workspace_bytes_ex": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                                      ctypes.POINTER(Plan), ctypes.POINTER(ctypes.c_size_t)]),
     "awq_linear": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,

@@ -8,6 +8,7 @@
 #include <stdlib.h>
 
 #include "../../include/awq.h"
+#include "../../include/awq_probe.h"
 #include "awq_launch.h"
 
 namespace {
@@ -204,8 +205,11 @@ int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scale
     return hip_status(awq::launch_fill_zero(y, M * n_out, (hipStream_t)stream));
   }
   if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
+  // y: 8-byte aligned wherever four outputs are stored at once (the gated
+  // prefill epilogue, and the reduction of split-K partials)
+  const bool y_by_four = r.path == 2 && (gated || r.split > 1);
   if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
-      !aligned(y, gated && r.path == 2 ? 8 : 2))
+      !aligned(y, y_by_four ? 8 : 2))
     return AWQ_ERR_ALIGN;
   if (r.ws_bytes) {
     if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
@@ -443,6 +447,11 @@ int awq_linear_workspace_bytes_ex(int64_t M, int64_t K, int64_t N, int group, co
 
 int awq_linear_workspace_bytes(int64_t M, int64_t K, int64_t N, int group, size_t* bytes) {
   return awq_linear_workspace_bytes_ex(M, K, N, group, nullptr, bytes);
+}
+
+size_t awq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int group) {
+  size_t bytes = 0;
+  return awq_linear_workspace_bytes(M, K, N, group, &bytes) == AWQ_OK ? bytes : SIZE_MAX;
 }
 
 int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
