@@ -229,3 +229,52 @@ def test_bench_workloads_sampled(awq, w):
     check_step(qkv[bs], kc[bs], vc[bs], lengths[bs], w.Hq, w.Hkv, w.rope, w.theta,
                (out[bs], k_after[bs], v_after[bs]), w.name)
     assert np.all(np.isfinite(out.astype(np.float32)))
+
+
+# The bench's attention workloads (L a power of two) with L - 1 cached
+# positions, so that L - 1 + 1 is a power of two; the automatic work split is
+# the same as at L (the same 32-position blocks).
+EXACT_WORKLOADS = [(w, w.L - 1) for w in __import__("synth").ATTENTION_WORKLOADS]
+
+
+@pytest.mark.parametrize("w,L", EXACT_WORKLOADS, ids=lambda a: getattr(a, "name", str(a)))
+def test_exact_case_bit_for_bit(awq, w, L):
+    # Every query 0 (every probability 1/(L+1)) and odd-integer values: the
+    # output is sum_j v_j / (L + 1), an fp16 number, and must equal the
+    # oracle's bit for bit. A dropped, repeated or misplaced cached position,
+    # a lost new token or a wrong kv head changes the bits (pinned on the CPU).
+    import synth
+    assert (L + 1) & L == 0
+    desc = awq.attention_desc(w.B, w.Hq, w.Hkv, w.D, (L + 1 + 31) // 32 * 32, L, rope=w.rope, theta=w.theta)
+    bench_desc = awq.attention_desc(w.B, w.Hq, w.Hkv, w.D, w.capacity, w.L, rope=w.rope, theta=w.theta)
+    plan = awq.attention_plan(desc)
+    assert plan == awq.attention_plan(bench_desc)
+    log(f"attention exact {w.name} L={L} plan={plan}")
+    qkv, kc, vc, lengths = synth.attention_exact_inputs(w, L, seed=2)
+    out, k_after, v_after = run_step(awq, qkv, kc, vc, lengths, w.Hq, w.Hkv, L, w.rope, w.theta)
+    y64, k_new, v_new = oracle.decode_step64(qkv, kc, vc, lengths, w.Hq, w.Hkv, w.D, w.theta, w.rope)
+    want = y64.astype(np.float16).view(np.uint16)
+    got = out.view(np.uint16)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{len(bad)} outputs differ, first at (b, head, d) = {tuple(bad[0])}"
+    for b in (0, w.B - 1):
+        assert np.array_equal(v_after[b][:, L].view(np.uint16), v_new[b].view(np.uint16))
+        assert np.array_equal(v_after[b][:, :L].view(np.uint16), vc[b][:, :L].view(np.uint16))
+        assert np.array_equal(k_after[b][:, :L].view(np.uint16), kc[b][:, :L].view(np.uint16))
+
+
+def test_workspace_shared_across_shapes(awq):
+    # One buffer for two calls: B = 1 with 4095 cached positions (32 units,
+    # 16 workgroups each: the larger buffer), then B = 8 with at most 31
+    # (256 units, whose counters lie where the first call's states were).
+    # Both outputs against the oracle; the buffer all zero after each call.
+    import torch
+    ws = awq.AttentionWorkspace(torch.device("cuda"))
+    for (B, lengths, S, seed) in ((1, [4095], 4096, 21), (8, [31, 0, 5, 30, 31, 17, 1, 29], 32, 22)):
+        desc = awq.attention_desc(B, 32, 32, 128, S, max(lengths))
+        log(f"attention shared workspace B={B} L={lengths} plan={awq.attention_plan(desc)} "
+            f"ws={awq.attention_workspace_bytes(desc)} buffer={None if ws.buf is None else ws.buf.numel()}")
+        qkv, kc, vc = _inputs(B, 32, 32, 128, S, seed=seed)
+        got = run_step(awq, qkv, kc, vc, lengths, 32, 32, max(lengths), "half", 1e4, workspace=ws)
+        check_step(qkv, kc, vc, lengths, 32, 32, "half", 1e4, got, f"shared workspace B={B}")
+        assert int(torch.count_nonzero(ws.buf)) == 0, "workspace not all zero after the call"

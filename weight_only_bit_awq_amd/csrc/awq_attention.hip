@@ -29,12 +29,14 @@
 //   * The rotation angles are computed once per workgroup in fp64 (rate
 //     theta^(-2i/D) times the position), kept as fp32 cos/sin in LDS.
 //   * The last workgroup of a unit to finish (an agent-scope counter in the
-//     workspace, returned to zero by that workgroup) merges the states in a
-//     fixed order, all its threads loading several states at once (one
-//     round trip to memory for up to 8 x 16 / heads-per-tile workgroups),
-//     adds the new token (its rotated key rounded to fp16,
-//     as it is stored, and its value), writes the fp16 output and, for the
-//     unit's first tile, appends the key and value to the caches.
+//     workspace) merges the states in a fixed order, all its threads loading
+//     several states at once (one round trip to memory for up to
+//     8 x 16 / heads-per-tile workgroups), adds the new token (its rotated
+//     key rounded to fp16, as it is stored, and its value), writes the fp16
+//     output and, for the unit's first tile, appends the key and value to
+//     the caches. It then
+//     returns the counter and the states it read to zero, so that the
+//     workspace is all zero between calls whatever their shapes.
 //   * Positions at or beyond a sequence's length are masked: their scores are
 //     replaced by -inf and their values by zero before the value product, so
 //     stale cache contents (even NaN patterns) never reach the output.
@@ -430,6 +432,18 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_decode_kernel(AttnParams
         kdst[i] = __builtin_bit_cast(uint16_t, ki);
         vdst[i * kAttnBlock] = __builtin_bit_cast(uint16_t, vi);
       }
+    }
+  }
+  // Leave the unit's part of the workspace as it was found, all zero: the
+  // counter, and the nsl states this call wrote (their hv head rows), which
+  // were all read above and consumed before the last barrier. A later call
+  // with another shape may place its counters where these states lie.
+  {
+    float* pu = p.part + (int64_t)unit * p.C * 16 * HS;
+    const int per_slot = hv * HS / 2;  // 8-byte stores per state
+    for (int e = tid; e < nsl * per_slot; e += kAttnWaves * 64) {
+      const int sl = e / per_slot, r = e - sl * per_slot;
+      coherent_store2(pu + (int64_t)sl * 16 * HS + 2 * r, 0.f, 0.f);
     }
   }
   if (tid == 0) __hip_atomic_store(p.counters + unit, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
