@@ -213,6 +213,25 @@ int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* sc
                   const awq_plan* plan, void* stream);
 
 /*
+ * awq_linear_noalloc: awq_linear_ex for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). It takes no workspace and allocates nothing: the fp32
+ * partial sums of a prefill plan that splits K go to a 64 MiB (67108864-byte)
+ * array the library holds on every GPU it is loaded on until the process
+ * ends. With plan NULL or split_k 0 the plan is awq_linear's automatic one
+ * with the K split lowered until split_k * M * N * 4 bytes fit in 64 MiB
+ * (down to no split, which needs none); an explicit split_k whose partials
+ * exceed 64 MiB returns AWQ_ERR_WORKSPACE before anything is enqueued. All
+ * calls on one GPU share the array and calls that overlap in time on one GPU
+ * (other streams, other threads) race on it; the array needs no clearing
+ * (every partial is written before it is read). Other arguments, alignment
+ * and errors as for awq_linear_ex.
+ */
+int awq_linear_noalloc(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                       const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
+                       uint16_t* y, const awq_plan* plan, void* stream);
+
+/*
  * awq_linear_timed: awq_linear_ex that also records two hipEvent_t handles
  * (passed as void*, either may be NULL): `start_event` at the start of the
  * call's first kernel and `stop_event` at the end of its last kernel

@@ -76,6 +76,9 @@ _SIGS = {
     "awq_linear_ex": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                      ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p,
                                      ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan), ctypes.c_void_p]),
+    "awq_linear_noalloc": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                          ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                          ctypes.c_void_p, ctypes.POINTER(Plan), ctypes.c_void_p]),
     "awq_linear_timed": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                         ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
                                         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(Plan),
@@ -323,6 +326,30 @@ def linear(x, qweight, scales, zeros, N: int, group: int = 128, out=None, worksp
     return out
 
 
+def linear_noalloc(x, qweight, scales, zeros, N: int, group: int = 128, out=None, plan=None):
+    """awq_linear without a workspace: split-K partials go to the library's
+    own 64 MiB device array (nothing is allocated by the library; ``out`` may
+    be passed in so that this call allocates nothing either)."""
+    torch = _torch()
+    _need(x, torch.float16, "x", 2)
+    _need(qweight, torch.int32, "qweight")
+    _need(scales, torch.float16, "scales", 2)
+    _need(zeros, torch.int32, "zeros", 2)
+    M, K = x.shape
+    if scales.shape != (K // group, N) or zeros.shape != (K // group, N // 8):
+        raise ValueError("scales must be [K/G, N] and zeros [K/G, N/8]")
+    if qweight.numel() < qweight_words(K, N):
+        raise ValueError("qweight is smaller than the device layout needs")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    else:
+        _need(out, torch.float16, "out", 2)
+    p = _plan(plan)
+    _check(library().awq_linear_noalloc(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), M, K,
+                                        N, group, out.data_ptr(), ctypes.byref(p) if p else None, _stream(x.device)))
+    return out
+
+
 def linear_silu_mul_plan(M: int, K: int, N: int, group: int = 128, plan=None) -> dict:
     p = _plan(plan) or Plan()
     _check(library().awq_linear_silu_mul_plan(M, K, N, group, ctypes.byref(p)))
@@ -531,6 +558,6 @@ def attention(qkv, k_cache, v_cache, lengths, q_heads: int, kv_heads: int, max_c
 
 __all__ = ["quantize_act_fp8", "linear_w4a8", "linear_w4a8_plan", "linear_w4a8_workspace_bytes", "attention", "attention_desc", "attention_plan", "attention_workspace_bytes", "kv_cache",
            "AttentionWorkspace", "library", "pack", "unpack", "pack_zeros", "dequant", "quantize", "linear", "linear_silu_mul",
-           "linear_silu_mul_plan", "linear_silu_mul_workspace_bytes", "linear_plan",
+           "linear_silu_mul_plan", "linear_silu_mul_workspace_bytes", "linear_plan", "linear_noalloc",
            "linear_workspace_bytes", "qweight_words", "Plan", "Workspace", "AWQError", "AWQLibraryMissing",
            "abi_version"]

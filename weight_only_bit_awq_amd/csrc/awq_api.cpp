@@ -69,7 +69,10 @@ bool gated_decode_fits(int64_t M, int64_t K, int G, const awq_plan& p) {
   return gated_decode_waves(M, K, G, p) > 0 || gated_stream_ok(M, p);
 }
 
-int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out, bool gated = false) {
+// ws_cap: a bound on the workspace (the library's own scratch for callers
+// that cannot allocate); an automatic K split shrinks until its partials fit.
+int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out, bool gated = false,
+                 size_t ws_cap = SIZE_MAX) {
   awq_plan p = {};
   if (in) p = *in;
   if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2 ||
@@ -180,6 +183,8 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (split > steps) split = steps > 0 ? steps : 1;
     out->split = split;
     out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, split, gated);
+    while (!p.split_k && out->split > 1 && out->ws_bytes > ws_cap)
+      out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, --out->split, gated);
   }
   return AWQ_OK;
 }
@@ -188,14 +193,18 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
 
 namespace {
 
+// noalloc: the split-K partials go to the library's static scratch (the
+// caller passes no workspace); nothing is allocated.
 int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
                int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes,
-               const awq_plan* plan, void* stream, void* start_event, void* stop_event, bool gated) {
+               const awq_plan* plan, void* stream, void* start_event, void* stop_event, bool gated,
+               bool noalloc = false) {
   int st = check_dims(M, K, N);
   if (st) return st;
   if ((st = check_layer(K, N, group))) return st;
   Resolved r;
-  if ((st = resolve_plan(M, K, N, group, plan, &r, gated))) return st;
+  if ((st = resolve_plan(M, K, N, group, plan, &r, gated, noalloc ? awq::kNoAllocScratchBytes : SIZE_MAX)))
+    return st;
   if (M == 0 || N == 0) return AWQ_OK;
   if (!y) return AWQ_ERR_NULL;
   const int64_t n_out = gated ? N / 2 : N;
@@ -211,6 +220,13 @@ int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scale
   if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
       !aligned(y, y_by_four ? 8 : 2))
     return AWQ_ERR_ALIGN;
+  if (r.ws_bytes && noalloc) {
+    if (r.ws_bytes > awq::kNoAllocScratchBytes) return AWQ_ERR_WORKSPACE;
+    float* p = nullptr;
+    if ((st = hip_status(awq::noalloc_scratch(&p)))) return st;
+    workspace = p;
+    workspace_bytes = awq::kNoAllocScratchBytes;
+  }
   if (r.ws_bytes) {
     if (!workspace || workspace_bytes < r.ws_bytes) return AWQ_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return AWQ_ERR_ALIGN;
@@ -504,6 +520,12 @@ int awq_stream_read(const void* buf, size_t bytes, void* sink, void* stream, voi
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros, int64_t M,
                int64_t K, int64_t N, int group, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
   return awq_linear_ex(x, qweight, scales, zeros, M, K, N, group, y, workspace, workspace_bytes, nullptr, stream);
+}
+
+int awq_linear_noalloc(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint32_t* zeros,
+                       int64_t M, int64_t K, int64_t N, int group, uint16_t* y, const awq_plan* plan, void* stream) {
+  return run_linear(x, qweight, scales, zeros, M, K, N, group, y, nullptr, 0, plan, stream, nullptr, nullptr, false,
+                    true);
 }
 
 int awq_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, uint8_t* x8, float* sx, void* stream) {

@@ -75,6 +75,14 @@ void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, double step_
 // workspace and the reduction applies the epilogue.
 size_t prefill_workspace_bytes(int M, int N, int splits, bool gated);
 bool prefill_fits(int K, int N);
+
+// Library-owned device memory for the split-K partials of callers that
+// cannot allocate: kNoAllocScratchBytes per device, shared by every such call
+// on that device. noalloc_scratch gives its address on the current device
+// (looked up once per device; allocates nothing).
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+constexpr int kNoAllocMaxDevices = 64;
+hipError_t noalloc_scratch(float** ptr);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
 // Sum of `splits` fp32 partials ws[s][mn] in increasing s, rounded to fp16.

@@ -31,10 +31,18 @@
 //     K steps and writes fp32 partial sums to ws[split][M][N]; a second
 //     kernel adds the splits in a fixed order and rounds once to fp16, so the
 //     result does not depend on scheduling.
+#include <atomic>
 #include <cmath>
 
 #include "awq_device.h"
 #include "awq_launch.h"
+
+// Device memory for callers that cannot allocate (awq_linear_noalloc): the
+// fp32 split-K partial sums live in this array, one copy per GPU the library
+// is loaded on, held until the process ends. Host code never passes its name
+// to a kernel (on the host it is only a stand-in for the device symbol); it
+// uses the device address from hipGetSymbolAddress, taken once per device.
+static __device__ __align__(256) float scratch[awq::kNoAllocScratchBytes / sizeof(float)];
 
 namespace awq {
 
@@ -453,6 +461,25 @@ size_t prefill_workspace_bytes(int M, int N, int splits, bool gated) {
 }
 
 bool prefill_fits(int K, int N) { return (size_t)((N + 15) / 16) * ((K + 127) / 128) * 1024 < ((size_t)1 << 31); }
+
+hipError_t noalloc_scratch(float** ptr) {
+  // one address per device, looked up with that device current (the caller's)
+  static std::atomic<float*> addr[kNoAllocMaxDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return hipErrorInvalidDevice;
+  float* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    void* v = nullptr;
+    e = hipGetSymbolAddress(&v, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    p = static_cast<float*>(v);
+    addr[dev].store(p, std::memory_order_release);
+  }
+  *ptr = p;
+  return hipSuccess;
+}
 
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L) {
   if (!prefill_fits(a.K, a.N)) return hipErrorInvalidValue;
