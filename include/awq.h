@@ -139,14 +139,16 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
  * Execution plan of awq_linear. Zero fields mean "choose automatically".
  *   path:    1 = decode path (dequantise in registers, MFMA 16x16x32, M <= 64),
  *            2 = prefill path (LDS-tiled dequant-then-MFMA GEMM, any M).
- *   split_k: prefill path: number of contiguous K ranges (1..16) computed
- *            by separate workgroups; their fp32 partial sums go to the
- *            workspace and a second kernel adds them in a fixed order and
- *            rounds once to fp16 (results do not depend on scheduling).
- *            Chosen automatically when the output has fewer tiles than the
- *            chip has workgroup slots (e.g. 512 x 5120 outputs). Must be 0
- *            or 1 on the decode path, which splits K over the waves of a
- *            workgroup instead.
+ *   split_k: number of contiguous K ranges (1..16, whole 128-row bands on
+ *            the decode path) computed by separate workgroups; their fp32
+ *            partial sums go to the workspace and a second kernel adds them
+ *            in a fixed order and rounds once to fp16 (results do not depend
+ *            on scheduling). Prefill path: chosen automatically when the
+ *            output has fewer tiles than the chip has workgroup slots (e.g.
+ *            512 x 5120 outputs). Decode path: streamed variant only
+ *            (x_stage 2); chosen automatically only for 24..32 rows on
+ *            narrow layers with a long K, since the second launch costs
+ *            more than the extra parallelism gains elsewhere.
  *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
  *            the K range of the workgroup's 16 columns and their partial sums
  *            are added through LDS in a fixed order.
@@ -176,7 +178,7 @@ int awq_linear_plan(int64_t M, int64_t K, int64_t N, int group, awq_plan* plan);
 
 /*
  * Workspace bytes awq_linear needs for this shape and plan: 0, or
- * split_k * M * N * 4 bytes of fp32 partial sums for a prefill plan with
+ * split_k * M * N * 4 bytes of fp32 partial sums for a plan with
  * split_k > 1 (the split-K of the layer, reduced in a fixed order; TinyChat
  * README "Usage" step 4, the W4A16 layer). The workspace needs no
  * initialisation (every byte used is written before it is read); it must be
@@ -198,8 +200,8 @@ size_t awq_linear_workspace_size(int64_t M, int64_t K, int64_t N, int group);
  * The W4A16 layer of TinyChat README "Usage" step 4 (--precision W4A16), the
  * generation-stage kernel of its "Speed Benchmarks". x and qweight 16-byte,
  * zeros 4-byte, scales 2-byte aligned; y 2-byte aligned, or 8-byte aligned
- * when the plan is a prefill plan with split_k > 1 (its reduction stores four
- * outputs at a time). The workspace as awq_linear_workspace_bytes gives it.
+ * when the plan has split_k > 1 (its reduction stores four outputs at a
+ * time). The workspace as awq_linear_workspace_bytes gives it.
  */
 int awq_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
@@ -216,7 +218,7 @@ int awq_linear_ex(const uint16_t* x, const uint32_t* qweight, const uint16_t* sc
  * awq_linear_noalloc: awq_linear_ex for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc). It takes no workspace and allocates nothing: the fp32
- * partial sums of a prefill plan that splits K go to a 64 MiB (67108864-byte)
+ * partial sums of a plan that splits K go to a 64 MiB (67108864-byte)
  * array the library holds on every GPU it is loaded on until the process
  * ends. With plan NULL or split_k 0 the plan is awq_linear's automatic one
  * with the K split lowered until split_k * M * N * 4 bytes fit in 64 MiB

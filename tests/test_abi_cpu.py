@@ -125,12 +125,25 @@ def test_validation_errors_before_launch(lib):
     p = awq.Plan()
     p.path, p.x_stage = 1, 1  # staged activations need M <= 16
     assert lib.awq_linear_plan(32, 4096, 4096, 128, ctypes.byref(p)) == -7
-    # no cross-workgroup split-K on the decode path
+    # a K split over workgroups on the decode path: streamed activations
+    # only, at most 16, partials in the workspace (refused without it)
     p = awq.Plan()
-    p.path, p.split_k = 1, 4
+    p.path, p.split_k, p.x_stage = 1, 4, 1
     need = ctypes.c_size_t(0)
     assert lib.awq_linear_workspace_bytes_ex(1, 4096, 4096, 128, ctypes.byref(p), ctypes.byref(need)) == -7
     assert lib.awq_linear_ex(fake, fake, fake, fake, 1, 4096, 4096, 128, fake, None, 0, ctypes.byref(p), None) == -7
+    p = awq.Plan()
+    p.path, p.split_k = 1, 17
+    assert lib.awq_linear_workspace_bytes_ex(1, 4096, 4096, 128, ctypes.byref(p), ctypes.byref(need)) == -7
+    p = awq.Plan()
+    p.path, p.split_k = 1, 4
+    assert lib.awq_linear_workspace_bytes_ex(8, 4096, 4096, 128, ctypes.byref(p), ctypes.byref(need)) == 0
+    assert need.value == 4 * 8 * 4096 * 4
+    assert awq.linear_plan(8, 4096, 4096, 128, {"path": 1, "split_k": 4})["x_stage"] == 2
+    assert awq.linear_plan(8, 256, 4096, 128, {"path": 1, "split_k": 4})["split_k"] == 2  # two bands
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 8, 4096, 4096, 128, fake, None, 0, ctypes.byref(p), None) == -5
+    assert lib.awq_linear_ex(fake, fake, fake, fake, 8, 4096, 4096, 128, ctypes.c_void_p(0x1002), fake, 1 << 30,
+                             ctypes.byref(p), None) == -4
     # prefill split-K: at most 16; a split plan without its workspace is refused before any launch
     p = awq.Plan()
     p.path, p.split_k = 2, 17
@@ -182,6 +195,11 @@ def test_batched_decode_plans(lib):
     assert p["tpw"] == 2
     p = awq.linear_plan(4, 14336, 4096, 128)                    # 256 tiles: staged, sixteen waves
     assert (p["x_stage"], p["waves"]) == (1, 16)
+    p = awq.linear_plan(32, 14336, 4096, 128)                   # long K, narrow, 32 rows: K split four ways
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (1, 2, 4, 8, 4)
+    assert awq.linear_workspace_bytes(32, 14336, 4096, 128) == 4 * 32 * 4096 * 4
+    assert awq.linear_plan(16, 14336, 4096, 128)["split_k"] == 1
+    assert awq.linear_plan(32, 4096, 4096, 128)["split_k"] == 1
     assert awq.linear_plan(48, 4096, 28672, 128)["path"] == 2   # wide layer above 32 rows: GEMM
     assert awq.linear_plan(48, 4096, 4096, 128)["path"] == 1
     with pytest.raises(awq.AWQError):                           # four tiles only with streamed activations

@@ -48,7 +48,11 @@ def sampled(q, z, s, cols):
     (20, 512, 96, 128, None), (300, 1024, 544, 64, None), (130, 2304, 160, 256, {"path": 2, "split_k": 3}),
     (8, 640, 64, 128, {"path": 2}), (513, 640, 96, 128, {"path": 2, "tile": 3}),
     (257, 640, 288, 64, {"path": 2, "tile": 1}), (600, 1024, 544, 128, {"path": 2, "tile": 2}),
-    (300, 4160, 96, 32, {"path": 2, "tile": 3, "split_k": 2})])
+    (300, 4160, 96, 32, {"path": 2, "tile": 3, "split_k": 2}),
+    # the streamed decode kernel with K split over workgroups
+    (16, 4096, 2048, 128, {"path": 1, "x_stage": 2, "tpw": 4, "split_k": 4}),
+    (32, 1216, 128, 64, {"path": 1, "tpw": 2, "waves": 8, "split_k": 3}),
+    (5, 3200, 96, 32, {"path": 1, "x_stage": 2, "tpw": 2, "split_k": 16})])
 def test_gated_matches_oracle(awq, M, K, N, G, plan):
     log(f"gated M={M} K={K} N={N} G={G} plan={plan}")
     q, z, s = synth.layer(K, N, G, seed=M + K + N)

@@ -39,6 +39,8 @@ PLANS = [
     (1, {"path": 1}), (1, {"path": 1, "waves": 4, "x_stage": 2}), (3, {"path": 1, "waves": 16, "x_stage": 1, "tpw": 2}),
     (8, {"path": 1, "waves": 4, "x_stage": 2, "tpw": 4}), (16, {"path": 1}), (33, {"path": 1}),
     (16, {"path": 1, "waves": 8, "x_stage": 2, "tpw": 2}),
+    (16, {"path": 1, "waves": 4, "x_stage": 2, "tpw": 2, "split_k": 3}),
+    (32, {"path": 1, "waves": 8, "x_stage": 2, "tpw": 4, "split_k": 2}),
     (80, {"path": 2, "tile": 1}), (130, {"path": 2, "tile": 3, "split_k": 3}), (70, {"path": 2, "tile": 2, "split_k": 2}),
 ]
 SHAPES = [(1024, 264, 128), (768, 136, 64), (640, 72, 32)]

@@ -95,6 +95,33 @@ def test_prefill_split_k(awq, M, K, N, G):
             check_close(run(awq, x, q, z, s, G, plan), y64, D, what=f"{plan}")
 
 
+@pytest.mark.parametrize("M,K,N,G", [(1, 4096, 256, 128), (16, 1216, 136, 64), (32, 3200, 64, 32),
+                                     (5, 14336, 48, 128), (64, 1024, 96, 128), (9, 4608, 264, 256),
+                                     (2, 384, 40, 128)])
+def test_decode_split_k(awq, M, K, N, G):
+    # the streamed decode kernel with K split over workgroups: fp32 partials
+    # in the workspace, added in a fixed order by the reduction kernel
+    log(f"decode split-K M={M} K={K} N={N} G={G}")
+    q, z, s = synth.layer(K, N, G, seed=M + K + 3)
+    x = synth.activations(M, K, seed=N + 3)
+    y64 = oracle.linear64(x, q, z, s, G)
+    D = oracle.l1_scale(x, q, z, s, G)
+    ran = 0
+    for waves in (4, 8):
+        for tpw in (1, 2, 4):
+            for split in (2, 3, 7, 16):
+                plan = {"path": 1, "x_stage": 2, "waves": waves, "tpw": tpw, "split_k": split}
+                try:
+                    used = awq.linear_plan(M, K, N, G, plan)
+                except awq.AWQError:
+                    continue  # four tiles per workgroup need M <= 32
+                log(f"  plan {plan} -> {used}")
+                assert used["split_k"] == min(split, -(-K // 128)) or used["split_k"] < split
+                check_close(run(awq, x, q, z, s, G, plan), y64, D, what=f"{plan}")
+                ran += 1
+    assert ran >= 8
+
+
 def _exact_case(M, K, N, G, seed=0):
     rng = np.random.default_rng(seed)
     q = rng.integers(0, 16, size=(K, N), dtype=np.uint8)
@@ -111,7 +138,9 @@ def _exact_case(M, K, N, G, seed=0):
                                   {"path": 1, "waves": 2, "x_stage": 1, "tpw": 1},
                                   {"path": 1, "waves": 1, "x_stage": 2}, {"path": 1, "waves": 4, "x_stage": 2},
                                   {"path": 2, "tile": 1}, {"path": 2, "tile": 2}, {"path": 2, "tile": 3},
-                                  {"path": 2, "tile": 2, "split_k": 3}, {"path": 2, "tile": 3, "split_k": 5}])
+                                  {"path": 2, "tile": 2, "split_k": 3}, {"path": 2, "tile": 3, "split_k": 5},
+                                  {"path": 1, "x_stage": 2, "waves": 4, "tpw": 2, "split_k": 3},
+                                  {"path": 1, "x_stage": 2, "waves": 8, "tpw": 4, "split_k": 6}])
 def test_exact_case_bitwise(awq, plan):
     M, K, N, G = 9, 768, 72, 128
     log(f"exact M={M} K={K} N={N} plan={plan}")
@@ -174,8 +203,8 @@ def test_k_zero_and_errors(awq):
     q, z, s = synth.layer(256, 16, 128)
     qw, zw, sd = upload_layer(q, z, s)
     xx = torch.zeros((1, 256), dtype=torch.float16, device="cuda")
-    with pytest.raises(awq.AWQError):
-        awq.linear(xx, qw, sd, zw, 16, 128, plan={"path": 1, "split_k": 4})
+    with pytest.raises(awq.AWQError):  # a K split needs the streamed decode variant
+        awq.linear(xx, qw, sd, zw, 16, 128, plan={"path": 1, "x_stage": 1, "split_k": 2})
     with pytest.raises(awq.AWQError):  # split plan, workspace too small
         awq.linear(torch.zeros((80, 256), dtype=torch.float16, device="cuda"), qw, sd, zw, 16, 128,
                    workspace=torch.zeros(64, dtype=torch.uint8, device="cuda"), plan={"path": 2, "split_k": 2})

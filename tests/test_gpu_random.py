@@ -63,6 +63,39 @@ def test_random_shapes_and_plans(awq, seed):
 
 
 @pytest.mark.parametrize("seed", range(12))
+def test_random_decode_split(awq, seed):
+    # the streamed decode kernel with K split over workgroups, plain and gated
+    rng = np.random.default_rng(3000 + seed)
+    G = int(rng.choice([32, 64, 128, 256]))
+    K = G * int(rng.integers(1, max(2, 4096 // G) + 1))
+    N = 32 * int(rng.integers(1, 20))
+    M = int(rng.choice([1, 2, 5, 8, 16, 17, 31, 32]))
+    gated = bool(rng.random() < 0.35)
+    plan = {"path": 1, "x_stage": 2, "waves": int(rng.choice([4, 8])), "tpw": int(rng.choice([1, 2, 4])),
+            "split_k": int(rng.choice([2, 3, 4, 6, 16]))}
+    planner = awq.linear_silu_mul_plan if gated else awq.linear_plan
+    try:
+        used = planner(M, K, N, G, plan)
+    except awq.AWQError as e:
+        assert e.status == -7, e
+        log(f"random split seed={seed} M={M} K={K} N={N} G={G} gated={gated} plan={plan}: rejected")
+        return
+    log(f"random split seed={seed} M={M} K={K} N={N} G={G} gated={gated} plan={plan} -> {used}")
+    q, z, s = synth.layer(K, N, G, seed=seed + 50)
+    x = synth.activations(M, K, seed=seed + 50)
+    qw, zw, sd = upload_layer(q, z, s)
+    if gated:
+        y = to_np16(awq.linear_silu_mul(x_dev(x), qw, sd, zw, N, G, plan=plan)).astype(np.float64)
+        ref = oracle.linear_silu_mul64(x, q, z, s, G)
+        E = oracle.silu_mul_scale(x, q, z, s, G)
+        assert np.all(np.isfinite(y))
+        assert float(np.max(np.abs(y - ref)[E > 0] / E[E > 0])) <= TOL
+    else:
+        y = to_np16(awq.linear(x_dev(x), qw, sd, zw, N, G, plan=plan))
+        check_close(y, oracle.linear64(x, q, z, s, G), oracle.l1_scale(x, q, z, s, G), what=f"seed {seed}")
+
+
+@pytest.mark.parametrize("seed", range(12))
 def test_random_w4a8(awq, seed):
     rng = np.random.default_rng(2000 + seed)
     G = int(rng.choice([32, 64, 128, 256]))

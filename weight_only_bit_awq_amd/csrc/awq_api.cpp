@@ -69,8 +69,17 @@ bool gated_decode_fits(int64_t M, int64_t K, int G, const awq_plan& p) {
   return gated_decode_waves(M, K, G, p) > 0 || gated_stream_ok(M, p);
 }
 
+// An automatic K split shrinks until its fp32 partials (split * M * N * 4
+// bytes, on either path) fit a workspace bound.
+void cap_split(Resolved* out, int64_t M, int64_t N, size_t ws_cap, bool automatic) {
+  while (automatic && out->split > 1 && out->ws_bytes > ws_cap) {
+    --out->split;
+    out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
+  }
+}
+
 // ws_cap: a bound on the workspace (the library's own scratch for callers
-// that cannot allocate); an automatic K split shrinks until its partials fit.
+// that cannot allocate).
 int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Resolved* out, bool gated = false,
                  size_t ws_cap = SIZE_MAX) {
   awq_plan p = {};
@@ -99,9 +108,12 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
   out->counter_bytes = 0;
   if (p.path == 1) {
     // The K range of a column tile is split over the waves of its workgroup
-    // and summed through LDS in a fixed order; there is no cross-workgroup
-    // split on this path.
-    if (p.split_k > 1) return AWQ_ERR_PLAN;
+    // and summed through LDS in a fixed order. The streamed variant can also
+    // split K over workgroups (split_k > 1): fp32 partials in the workspace,
+    // added in a fixed order by a second kernel.
+    if (p.split_k > 16) return AWQ_ERR_PLAN;
+    if (p.split_k > 1 && p.x_stage == 1) return AWQ_ERR_PLAN;
+    if (p.split_k > 1 && !p.x_stage) p.x_stage = 2;
     if (p.waves && p.waves != 1 && p.waves != 2 && p.waves != 4 && p.waves != 8 && p.waves != 16)
       return AWQ_ERR_PLAN;
     if (p.tpw > 4 || p.tpw == 3) return AWQ_ERR_PLAN;
@@ -125,9 +137,13 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
         int tw = p.tpw ? p.tpw : (NH >= 448 && NH % 2 == 0 && (M <= 16 || G >= 64)) ? 4 : 2;
         if (tw == 4 && NH % 2) return AWQ_ERR_PLAN;
         out->waves = p.waves ? p.waves : 4, out->tpw = tw, out->x_stage = 2;
+        out->split = awq::decode_splits((int)K, p.split_k ? p.split_k : 1);
       } else {
         return AWQ_ERR_PLAN;
       }
+      if (out->split > 1 && out->x_stage != 2) return AWQ_ERR_PLAN;
+      out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
+      cap_split(out, M, N, ws_cap, p.split_k == 0);
       return AWQ_OK;
     }
     int waves = p.waves;
@@ -135,7 +151,15 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
-    if (!p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
+    int auto_split = 1;
+    if (!p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 24 && M <= 32 && NT <= 512 && KT >= 64) {
+      // Many rows on a narrow layer with a long K (e.g. the LLaMA-3-8B down
+      // projection, 14336 x 4096, at M = 32): four K ranges over workgroups
+      // of eight waves and four tiles, partials added by the reduction
+      // kernel (measured 29.7 -> 19.6 us; at M <= 16 or on shorter K the
+      // second launch costs more than it saves).
+      x_stage = 2, waves = 8, auto_split = 4;
+    } else if (!p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
       // Batched rows on layers of 384 or more tiles: the streamed variant,
       // with adjacent tiles sharing each band's activation loads, beats
       // staging the activations per workgroup (measured on the LLaMA-3-8B
@@ -165,12 +189,20 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       if (p.tpw > 1 && !multi) return AWQ_ERR_PLAN;
       // (four tiles of 32 rows with four groups per band hold too many
       // registers: two there)
-      tpw = p.tpw ? p.tpw : !multi ? 1 : (NT >= 896 && (M <= 16 || G >= 64)) ? 4 : NT >= 384 ? 2 : 1;
+      tpw = p.tpw ? p.tpw
+                  : !multi                                      ? 1
+                  : auto_split > 1                              ? 4
+                  : (NT >= 896 && (M <= 16 || G >= 64))         ? 4
+                  : NT >= 384                                   ? 2
+                                                                : 1;
     }
     if (p.tile) return AWQ_ERR_PLAN;
     out->waves = waves;
     out->tpw = tpw;
     out->x_stage = x_stage;
+    if (p.split_k > 1 && x_stage != 2) return AWQ_ERR_PLAN;
+    out->split = x_stage == 2 ? awq::decode_splits((int)K, p.split_k ? p.split_k : auto_split) : 1;
+    out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
   } else {
     if (p.waves || p.tpw || p.x_stage) return AWQ_ERR_PLAN;
     if (!awq::prefill_fits((int)K, (int)N)) return AWQ_ERR_SHAPE;
@@ -183,9 +215,8 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (split > steps) split = steps > 0 ? steps : 1;
     out->split = split;
     out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, split, gated);
-    while (!p.split_k && out->split > 1 && out->ws_bytes > ws_cap)
-      out->ws_bytes = awq::prefill_workspace_bytes((int)M, (int)N, --out->split, gated);
   }
+  cap_split(out, M, N, ws_cap, p.split_k == 0);
   return AWQ_OK;
 }
 
@@ -216,7 +247,7 @@ int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scale
   if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
   // y: 8-byte aligned wherever four outputs are stored at once (the gated
   // prefill epilogue, and the reduction of split-K partials)
-  const bool y_by_four = r.path == 2 && (gated || r.split > 1);
+  const bool y_by_four = (r.path == 2 && gated) || r.split > 1;
   if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(scales, 2) || !aligned(zeros, 4) ||
       !aligned(y, y_by_four ? 8 : 2))
     return AWQ_ERR_ALIGN;
@@ -236,7 +267,7 @@ int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scale
   awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
   const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
   if (r.path == 1) {
-    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1, gated};
+    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1, gated, r.split, static_cast<float*>(workspace)};
     return hip_status(awq::launch_decode(a, cfg, L));
   }
   return hip_status(awq::launch_prefill(a, r.tile, r.split, static_cast<float*>(workspace), gated, L));

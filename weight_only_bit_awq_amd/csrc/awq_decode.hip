@@ -379,16 +379,25 @@ __device__ __forceinline__ void consume_bundle(const Bundle<MT, GPT, TW>& b, f4 
 // them for its bands, so the activations it loads serve TW tiles. GATED (TW =
 // 2 or 4): TW/2 adjacent tiles of the gate half and the same tiles of the up
 // half, stored as y[m, n] = silu(gate) * up ([M, N/2]).
+// K split (part != nullptr): work id u = split * n_groups + group covers the
+// bands [split * kps, (split + 1) * kps) of its column group and stores its
+// fp32 sums at part[split][row][column] (gated: the gate sums at the output's
+// column, the up sums N/2 further); a second kernel adds the splits in order.
+// Work ids of one split are adjacent, so the workgroups that run together on
+// one XCD share that split's activation slice in L2.
 template <int MT, int GPT, int WAVES, int DEPTH, int TW, bool GATED = false>
 __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_t* __restrict__ x,
                                                                    const u4* __restrict__ qw,
                                                                    const uint16_t* __restrict__ scales,
                                                                    const uint32_t* __restrict__ zeros,
                                                                    uint16_t* __restrict__ y, int M, int K, int N,
-                                                                   int G, int NT) {
+                                                                   int G, int NT, float* __restrict__ part,
+                                                                   int n_groups, int kps) {
   static_assert(!GATED || TW == 2 || TW == 4, "gated: gate tiles and as many up tiles");
   constexpr int TH = GATED ? TW / 2 : TW;  // gate tiles (gated) or tiles per workgroup
-  const int t0 = xcd_remap(blockIdx.x, gridDim.x) * TH;
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = u / n_groups;
+  const int t0 = (u - split * n_groups) * TH;
   // column tile of the workgroup's tile tt: the up tiles lie NT/2 after the gate tiles
   auto tile_of = [&](int tt) { return GATED && tt >= TH ? NT / 2 + t0 + (tt - TH) : t0 + tt; };
   const int lane = threadIdx.x & 63;
@@ -422,8 +431,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
   const DecodeConsts kc = decode_consts();
   const int lcol = lane & 15;
 
-  const int n_my = KT > w ? (KT - w + WAVES - 1) / WAVES : 0;
-  const int last = max(w + WAVES * (n_my - 1), 0);
+  // this workgroup's bands [kt0, kt1), never empty; wave w takes kt0 + w,
+  // kt0 + w + WAVES, ...
+  const int kt0 = split * kps, kt1 = min(KT, kt0 + kps);
+  const int n_my = kt1 - kt0 > w ? (kt1 - kt0 - w + WAVES - 1) / WAVES : 0;
+  const int last = kt0 + max(w + WAVES * (n_my - 1), 0);
 
   f4 acc[TW][MT];
 #pragma unroll
@@ -433,14 +445,14 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
 
   Bundle<MT, GPT, TW> buf[DEPTH];
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT, TW>(buf[d], c, min(w + WAVES * d, last));
+  for (int d = 0; d < DEPTH; ++d) load_bundle<MT, GPT, TW>(buf[d], c, min(kt0 + w + WAVES * d, last));
   const int rounds = max((n_my + DEPTH - 1) / DEPTH, 1);
   for (int r = 0; r < rounds - 1; ++r) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
       const int i = r * DEPTH + d;
       consume_bundle<MT, GPT, TW>(buf[d], acc, lcol, 1.f, kc);
-      load_bundle<MT, GPT, TW>(buf[d], c, min(w + WAVES * (i + DEPTH), last));
+      load_bundle<MT, GPT, TW>(buf[d], c, min(kt0 + w + WAVES * (i + DEPTH), last));
     }
   }
 #pragma unroll
@@ -487,9 +499,16 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
         const int ol = o & 63, mr = o >> 6;
         const int row = 16 * (mr >> 2) + 4 * (ol >> 4) + (mr & 3);
         const int cc = 16 * (t0 + pt) + (ol & 15);
-        const float g = v[0][i], u = v[1][i];
-        if (o < OUTS && row < M && cc < NO)
-          y[(int64_t)row * NO + cc] = __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + expf(-g)) * u));
+        const float g = v[0][i], up = v[1][i];
+        if (o < OUTS && row < M && cc < NO) {
+          if (part) {
+            float* pr = part + ((int64_t)split * M + row) * N;
+            pr[cc] = g;
+            pr[NO + cc] = up;
+          } else {
+            y[(int64_t)row * NO + cc] = __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + expf(-g)) * up));
+          }
+        }
       }
     }
   } else if constexpr (WAVES > 1) {
@@ -510,7 +529,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
         const int ol = o & 63, mr = o >> 6;
         const int row = 16 * (mr >> 2) + 4 * (ol >> 4) + (mr & 3);
         const int cc = 16 * (t0 + tt) + (ol & 15);
-        if (row < M && cc < N) y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        if (row < M && cc < N) {
+          if (part)
+            part[((int64_t)split * M + row) * N + cc] = v;
+          else
+            y[(int64_t)row * N + cc] = __builtin_bit_cast(uint16_t, (_Float16)v);
+        }
       }
     }
   } else {
@@ -523,7 +547,12 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
           const int row = 16 * mt + 4 * h + r;
           const int col = 16 * (t0 + tt) + lcol;
           const float v = acc[tt][mt][r];
-          if (row < M && col < N) y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+          if (row < M && col < N) {
+            if (part)
+              part[((int64_t)split * M + row) * N + col] = v;
+            else
+              y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)v);
+          }
         }
   }
 }
@@ -624,73 +653,103 @@ hipError_t launch_staged_t(const LinearArgs& a, int waves, const StagedSizes& z,
   return launch_staged_g<TM, 0>(a, waves, z, L);
 }
 
+// A split of the K range into `splits` ranges of whole bands (every range
+// non-empty): bands per range, and the number of ranges that gives.
+struct KSplit {
+  int kps, splits;
+};
+KSplit k_split(int K, int splits) {
+  const int KT = (K + 127) / 128;
+  const int s = splits < 1 ? 1 : (splits > KT ? KT : splits);
+  const int kps = (KT + s - 1) / s;
+  return KSplit{kps, (KT + kps - 1) / kps};
+}
+
+// With splits > 1 the kernel writes fp32 partials to ws[split][M][N] and the
+// prefill path's fixed-order reduction adds them (and applies the gated
+// epilogue); `L.start` is recorded at the first kernel, `L.stop` at the last.
+template <typename F>
+hipError_t launch_stream_split(F k, int groups, int waves, const LinearArgs& a, int splits, float* ws, bool gated,
+                               const Launch& L) {
+  const int NT = (a.N + 15) / 16;
+  const KSplit ks = k_split(a.K, splits);
+  float* part = ks.splits > 1 ? ws : nullptr;
+  if (ks.splits > 1 && !ws) return hipErrorInvalidValue;
+  const Launch first{L.stream, L.start, part ? nullptr : L.stop};
+  hipError_t e = launch_kernel(k, dim3((unsigned)(groups * ks.splits)), dim3(64 * waves), 0, first, a.x,
+                               reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M, a.K, a.N, a.G, NT,
+                               part, groups, ks.kps);
+  if (e != hipSuccess || !part) return e;
+  return launch_prefill_reduce(part, a.y, a.M, a.N, ks.splits, gated, Launch{L.stream, nullptr, L.stop});
+}
+
 template <int MT, int GPT, int WAVES, int TW>
-hipError_t launch_stream_k(const LinearArgs& a, const Launch& L) {
+hipError_t launch_stream_k(const LinearArgs& a, int splits, float* ws, const Launch& L) {
   // bands in flight per wave: fewer when a band carries more registers
   constexpr int DEPTH = TW == 1 ? (MT == 1 ? 4 : (MT == 2 ? 3 : 2)) : 2;
   const int NT = (a.N + 15) / 16;
-  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, DEPTH, TW>, dim3((unsigned)((NT + TW - 1) / TW)),
-                       dim3(64 * WAVES), 0, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M,
-                       a.K, a.N, a.G, NT);
+  return launch_stream_split(decode_stream_kernel<MT, GPT, WAVES, DEPTH, TW>, (NT + TW - 1) / TW, WAVES, a, splits,
+                             ws, false, L);
 }
 
 template <int MT, int GPT, int WAVES, int TW>
-hipError_t launch_stream_gated_k(const LinearArgs& a, const Launch& L) {
+hipError_t launch_stream_gated_k(const LinearArgs& a, int splits, float* ws, const Launch& L) {
   const int NT = (a.N + 15) / 16;
   if ((NT / 2) % (TW / 2)) return hipErrorInvalidValue;  // whole groups of gate tiles
-  return launch_kernel(decode_stream_kernel<MT, GPT, WAVES, 2, TW, true>, dim3((unsigned)(NT / TW)),
-                       dim3(64 * WAVES), 0, L, a.x, reinterpret_cast<const u4*>(a.qw), a.scales, a.zeros, a.y, a.M,
-                       a.K, a.N, a.G, NT);
+  return launch_stream_split(decode_stream_kernel<MT, GPT, WAVES, 2, TW, true>, NT / TW, WAVES, a, splits, ws, true,
+                             L);
 }
 
 template <int MT, int GPT>
-hipError_t launch_stream_gated(const LinearArgs& a, int waves, int tw, const Launch& L) {
-  if (waves == 4 && tw == 2) return launch_stream_gated_k<MT, GPT, 4, 2>(a, L);
-  if (waves == 4 && tw == 4) return launch_stream_gated_k<MT, GPT, 4, 4>(a, L);
-  if (waves == 8 && tw == 2) return launch_stream_gated_k<MT, GPT, 8, 2>(a, L);
-  if (waves == 8 && tw == 4) return launch_stream_gated_k<MT, GPT, 8, 4>(a, L);
+hipError_t launch_stream_gated(const LinearArgs& a, int waves, int tw, int splits, float* ws, const Launch& L) {
+  if (waves == 4 && tw == 2) return launch_stream_gated_k<MT, GPT, 4, 2>(a, splits, ws, L);
+  if (waves == 4 && tw == 4) return launch_stream_gated_k<MT, GPT, 4, 4>(a, splits, ws, L);
+  if (waves == 8 && tw == 2) return launch_stream_gated_k<MT, GPT, 8, 2>(a, splits, ws, L);
+  if (waves == 8 && tw == 4) return launch_stream_gated_k<MT, GPT, 8, 4>(a, splits, ws, L);
   return hipErrorInvalidValue;
 }
 
 template <int MT>
-hipError_t launch_stream_gated_g(const LinearArgs& a, int waves, int tw, const Launch& L) {
-  if (a.G == 32) return launch_stream_gated<MT, 4>(a, waves, tw, L);
-  if (a.G == 64) return launch_stream_gated<MT, 2>(a, waves, tw, L);
-  if (a.G == 128) return launch_stream_gated<MT, 1>(a, waves, tw, L);
-  return launch_stream_gated<MT, 0>(a, waves, tw, L);
+hipError_t launch_stream_gated_g(const LinearArgs& a, int waves, int tw, int splits, float* ws, const Launch& L) {
+  if (a.G == 32) return launch_stream_gated<MT, 4>(a, waves, tw, splits, ws, L);
+  if (a.G == 64) return launch_stream_gated<MT, 2>(a, waves, tw, splits, ws, L);
+  if (a.G == 128) return launch_stream_gated<MT, 1>(a, waves, tw, splits, ws, L);
+  return launch_stream_gated<MT, 0>(a, waves, tw, splits, ws, L);
 }
 
 template <int MT, int GPT, int WAVES>
-hipError_t launch_stream_t(const LinearArgs& a, int tw, const Launch& L) {
+hipError_t launch_stream_t(const LinearArgs& a, int tw, int splits, float* ws, const Launch& L) {
   if constexpr (MT <= 2 && (WAVES == 4 || WAVES == 8)) {
-    if (tw == 2) return launch_stream_k<MT, GPT, WAVES, 2>(a, L);
-    if (tw == 4) return launch_stream_k<MT, GPT, WAVES, 4>(a, L);
+    if (tw == 2) return launch_stream_k<MT, GPT, WAVES, 2>(a, splits, ws, L);
+    if (tw == 4) return launch_stream_k<MT, GPT, WAVES, 4>(a, splits, ws, L);
   }
   if (tw != 1) return hipErrorInvalidValue;
-  return launch_stream_k<MT, GPT, WAVES, 1>(a, L);
+  return launch_stream_k<MT, GPT, WAVES, 1>(a, splits, ws, L);
 }
 
 template <int MT, int GPT>
-hipError_t launch_stream_w(const LinearArgs& a, int waves, int tw, const Launch& L) {
+hipError_t launch_stream_w(const LinearArgs& a, int waves, int tw, int splits, float* ws, const Launch& L) {
   switch (waves) {
-    case 1: return launch_stream_t<MT, GPT, 1>(a, tw, L);
-    case 2: return launch_stream_t<MT, GPT, 2>(a, tw, L);
-    case 4: return launch_stream_t<MT, GPT, 4>(a, tw, L);
-    case 8: return launch_stream_t<MT, GPT, 8>(a, tw, L);
-    case 16: return launch_stream_t<MT, GPT, 16>(a, tw, L);
+    case 1: return launch_stream_t<MT, GPT, 1>(a, tw, splits, ws, L);
+    case 2: return launch_stream_t<MT, GPT, 2>(a, tw, splits, ws, L);
+    case 4: return launch_stream_t<MT, GPT, 4>(a, tw, splits, ws, L);
+    case 8: return launch_stream_t<MT, GPT, 8>(a, tw, splits, ws, L);
+    case 16: return launch_stream_t<MT, GPT, 16>(a, tw, splits, ws, L);
   }
   return hipErrorInvalidValue;
 }
 
 template <int MT>
-hipError_t launch_stream_g(const LinearArgs& a, int waves, int tw, const Launch& L) {
-  if (a.G == 32) return launch_stream_w<MT, 4>(a, waves, tw, L);
-  if (a.G == 64) return launch_stream_w<MT, 2>(a, waves, tw, L);
-  if (a.G == 128) return launch_stream_w<MT, 1>(a, waves, tw, L);
-  return launch_stream_w<MT, 0>(a, waves, tw, L);
+hipError_t launch_stream_g(const LinearArgs& a, int waves, int tw, int splits, float* ws, const Launch& L) {
+  if (a.G == 32) return launch_stream_w<MT, 4>(a, waves, tw, splits, ws, L);
+  if (a.G == 64) return launch_stream_w<MT, 2>(a, waves, tw, splits, ws, L);
+  if (a.G == 128) return launch_stream_w<MT, 1>(a, waves, tw, splits, ws, L);
+  return launch_stream_w<MT, 0>(a, waves, tw, splits, ws, L);
 }
 
 }  // namespace
+
+int decode_splits(int K, int splits) { return k_split(K, splits).splits; }
 
 bool decode_staged_fits(int M, int K, int G, int waves, int tpw) {
   if (M > 16 || waves < 2 || (tpw != 1 && tpw != 2)) return false;
@@ -703,8 +762,8 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
     // gate and up tiles paired in one workgroup
     if (a.N % 32) return hipErrorInvalidValue;
     if (!cfg.staged) {
-      if (a.M <= 16) return launch_stream_gated_g<1>(a, cfg.waves, cfg.tpw, L);
-      if (a.M <= 32) return launch_stream_gated_g<2>(a, cfg.waves, cfg.tpw, L);
+      if (a.M <= 16) return launch_stream_gated_g<1>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
+      if (a.M <= 32) return launch_stream_gated_g<2>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
       return hipErrorInvalidValue;
     }
     if (cfg.waves < 2 || !decode_staged_fits(a.M, a.K, a.G, cfg.waves, 1)) return hipErrorInvalidValue;
@@ -716,9 +775,9 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
     if (cfg.tpw == 2) return launch_staged_t<2>(a, cfg.waves, z, L);
     return launch_staged_t<1>(a, cfg.waves, z, L);
   }
-  if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, cfg.tpw, L);
-  if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, cfg.tpw, L);
-  if (a.M <= 64) return launch_stream_g<4>(a, cfg.waves, cfg.tpw, L);
+  if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
+  if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
+  if (a.M <= 64) return launch_stream_g<4>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
   return hipErrorInvalidValue;
 }
 

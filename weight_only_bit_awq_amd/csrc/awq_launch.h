@@ -56,9 +56,14 @@ struct DecodeConfig {
   int waves;
   int tpw;
   bool staged;
-  bool gated;  // y[M, N/2] = silu(x W[:, :N/2]) * (x W[:, N/2:]); staged only, N % 32 == 0
+  bool gated;  // y[M, N/2] = silu(x W[:, :N/2]) * (x W[:, N/2:]); N % 32 == 0
+  int splits;  // streamed: K split over workgroups (fp32 partials in ws, then the fixed-order reduction)
+  float* ws;
 };
 bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
+// Splits a streamed decode plan actually runs with (whole bands per split,
+// every split non-empty).
+int decode_splits(int K, int splits);
 hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Launch& L);
 
 // Prefill path: dequantise-then-MFMA GEMM; `tile` selects the workgroup tile
@@ -85,8 +90,10 @@ constexpr int kNoAllocMaxDevices = 64;
 hipError_t noalloc_scratch(float** ptr);
 hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, bool gated, const Launch& L);
 
-// Sum of `splits` fp32 partials ws[s][mn] in increasing s, rounded to fp16.
-hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int64_t mn, int splits, const Launch& L);
+// Sum of `splits` fp32 partials ws[s][M][N] in increasing s, rounded to
+// fp16 into y [M, N]; gated: y [M, N/2] = silu(sum of the gate half) * (sum
+// of the up half).
+hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int M, int N, int splits, bool gated, const Launch& L);
 
 // W4A8-FP8: per-token FP8 (E4M3) activation quantiser, and the layer on the
 // FP8 matrix cores (G a multiple of 128). The workspace holds the FP8

@@ -390,7 +390,11 @@ hipError_t launch_prefill_k(const LinearArgs& a, int splits, float* ws, bool gat
 
 }  // namespace
 
-hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int64_t mn, int splits, const Launch& L) {
+hipError_t launch_prefill_reduce(float* ws, uint16_t* y, int M, int N, int splits, bool gated, const Launch& L) {
+  const int64_t mn = (int64_t)M * N;
+  if (gated)
+    return launch_kernel(prefill_reduce_silu_mul_kernel, dim3((unsigned)((mn / 2 / 4 + 255) / 256)), dim3(256), 0, L,
+                         static_cast<const float*>(ws), y, M, N, splits);
   return launch_kernel(prefill_reduce_kernel, dim3((unsigned)((mn / 4 + 255) / 256)), dim3(256), 0, L,
                        static_cast<const float*>(ws), y, mn, splits);
 }

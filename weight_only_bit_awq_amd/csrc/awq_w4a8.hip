@@ -400,8 +400,7 @@ hipError_t launch_w4a8_tile(const uint8_t* x8, const float* sx, const LinearArgs
                                a.scales, a.zeros, a.y, used > 1 ? ws : (float*)nullptr, a.M, a.K, a.N, a.G, NT,
                                n_mtiles, n_tiles, split_steps, qw_bytes);
   if (e != hipSuccess || used <= 1) return e;
-  const int64_t mn = (int64_t)a.M * a.N;
-  return launch_prefill_reduce(ws, a.y, mn, used, Launch{L.stream, nullptr, L.stop});
+  return launch_prefill_reduce(ws, a.y, a.M, a.N, used, false, Launch{L.stream, nullptr, L.stop});
 }
 }  // namespace
 
