@@ -650,6 +650,108 @@ def cpu_baseline(workload, seconds):
     }
 
 
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]))
+    except Exception:
+        return 1
+
+
+def _oracle_linear_chunked(x, q, z, s, G, max_bytes=2 << 30):
+    """The oracle's layer over contiguous K chunks of whole groups, each
+    dequantised to at most `max_bytes` of fp64 (same arithmetic as
+    oracle.linear64: fp64 dequantisation, fp64 product, summed over chunks)."""
+    import numpy as np
+
+    import oracle
+    K, N = q.shape
+    rows = max(G, (max_bytes // (8 * N)) // G * G)
+    y = np.zeros((x.shape[0], N))
+    for k0 in range(0, K, rows):
+        k1 = min(K, k0 + rows)
+        y += oracle.linear64(x[:, k0:k1], q[k0:k1], z[k0 // G:k1 // G], s[k0 // G:k1 // G], G)
+    return y
+
+
+def cpu_baseline_configs(seconds_small=3.0):
+    """The fp64 oracle on the host cores for the other workloads, in the GPU
+    metric's units, each leg bounded to a few seconds of CPU work:
+    the single 4096 x 4096 layer (M = 1, full shape, repeated); the
+    LLaMA-3-8B layer at every M of its sweep (one full pass each); the
+    LLaMA-2-13B prefill layer at M = 512 and 2048 on a column slice of every
+    shape (1/8 of N), scaled to the full width (extrapolated); one
+    Falcon-180B-shaped layer (four linears, full shapes) with the
+    dequantisation taken in K chunks of at most 2 GB, times 80 layers
+    (extrapolated)."""
+    import numpy as np
+
+    import oracle
+    import synth
+    threads = _blas_threads()
+    out = {"kind": "oracle", "cores": threads,
+           "what": "numpy fp64 dequantise + BLAS matmul on the host cores (BLAS threads = cores; elementwise "
+                   "steps single-threaded); same generated bytes as the parity tests (seeded numpy)"}
+    # config: single layer 4096 x 4096, M = 1
+    w0 = synth.SINGLE_4096
+    sh = w0.shapes[0]
+    q, z, s = synth.layer(sh.K, sh.N, w0.G, seed=0)
+    x = synth.activations(1, sh.K, seed=0)
+    n, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds_small:
+        oracle.linear64(x, q, z, s, w0.G)
+        n += 1
+    dt = time.perf_counter() - t0
+    out[w0.name] = {"value": round(n * weight_set_bytes(sh.K, sh.N, w0.G) / dt / 1e9, 4), "unit": "GB/s",
+                    "sample": f"{n} call(s) of the full 4096 x 4096 layer at M=1, {dt:.1f} s"}
+    # config: LLaMA-3-8B layer, M = 1 .. 32, one full pass per M
+    w2 = synth.LLAMA3_8B_SWEEP
+    lay = [synth.layer(sh.K, sh.N, w2.G, seed=0, layer_id=i, scales=w2.scales, lo=w2.lo, hi=w2.hi)
+           for i, sh in enumerate(w2.shapes)]
+    per_m = {}
+    for M in w2.Ms:
+        t0 = time.perf_counter()
+        for i, (sh, (q, z, s)) in enumerate(zip(w2.shapes, lay)):
+            oracle.linear64(synth.activations(M, sh.K, seed=0, stream=i), q, z, s, w2.G)
+        dt = time.perf_counter() - t0
+        wb = sum(weight_set_bytes(sh.K, sh.N, w2.G) for sh in w2.shapes)
+        per_m[f"M={M}"] = {"value": round(wb / dt / 1e9, 4), "unit": "GB/s", "seconds": round(dt, 2)}
+    out[w2.name] = {"per_M": per_m, "sample": "one pass over the four full-shape linears per M"}
+    del lay
+    # config: LLaMA-2-13B prefill, column slice of 1/8 of N per shape
+    w3 = synth.LLAMA2_13B_PREFILL
+    per_m = {}
+    for M in w3.Ms:
+        flop, dt = 0.0, 0.0
+        for i, sh in enumerate(w3.shapes):
+            n8 = sh.N // 8
+            q, z, s = synth.layer(sh.K, n8, w3.G, seed=0, layer_id=i)
+            x = synth.activations(M, sh.K, seed=0, stream=i, outlier_frac=w3.outlier_frac)
+            t0 = time.perf_counter()
+            oracle.linear64(x, q, z, s, w3.G)
+            dt += time.perf_counter() - t0
+            flop += 2.0 * M * sh.K * sh.N
+        per_m[f"M={M}"] = {"value": round(flop / (8 * dt) / 1e9, 3), "unit": "GFLOP/s", "extrapolated": True,
+                           "seconds_measured": round(dt, 2)}
+    out[w3.name] = {"per_M": per_m, "sample": "each shape on 1/8 of its columns (full K, full M), time x 8"}
+    # config: Falcon-180B, one layer, K-chunked, x 80
+    w4 = synth.FALCON_180B_STACK
+    dt, wb = 0.0, 0
+    for i, sh in enumerate(w4.shapes):
+        q, z, s = synth.layer(sh.K, sh.N, w4.G, seed=0, layer_id=i)
+        x = synth.activations(1, sh.K, seed=0, stream=i)
+        t0 = time.perf_counter()
+        _oracle_linear_chunked(x, q, z, s, w4.G)
+        dt += time.perf_counter() - t0
+        wb += weight_set_bytes(sh.K, sh.N, w4.G)
+        del q, z, s
+    out[w4.name] = {"value": round(wb / dt / 1e9, 4), "unit": "GB/s", "extrapolated": True,
+                    "ms_per_step": round(dt * w4.layers * 1e3, 1),
+                    "sample": f"one full layer (four linears, {wb / 1e9:.2f} GB of weights) at M=1 with K-chunked "
+                              f"fp64 dequantisation (<= 2 GB per chunk), {dt:.1f} s, x {w4.layers} layers"}
+    return out
+
+
 def _short(name):
     return name.split("(")[0].replace("void ", "")
 
@@ -1137,9 +1239,13 @@ def main():
         eprint("[bench] copy calibration: 1 GiB device copy done")
 
     cpu = None
+    cpu_configs = None
     if not args.no_cpu_baseline:
         eprint(f"[bench] timing the CPU oracle for about {args.cpu_seconds:.0f} s")
         cpu = cpu_baseline(wl, args.cpu_seconds)
+        eprint("[bench] timing the CPU oracle on the other workloads")
+        cpu_configs = cpu_baseline_configs()
+        eprint("[bench] CPU oracle: " + json.dumps({k: v for k, v in cpu_configs.items() if isinstance(v, dict)})[:400])
 
     out = {
         "metric": "W4A16 GEMV weight GB/s (% HBM peak) at M=1; GEMM TFLOP/s at M=2048",
@@ -1173,6 +1279,7 @@ def main():
         "prefill": prefill,
         "w4a8": w4a8,
         "cpu_baseline": cpu,
+        "cpu_baseline_configs": cpu_configs,
     }
     print(json.dumps(out), flush=True)
 
