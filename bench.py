@@ -364,9 +364,15 @@ def decode_sweep(awq, lib, torch, hip, wl, dev, seed, layers=8, reps=3):
         layer_ms = sum(sum(v) / len(v) for v in t.values())
         wb = sum(weight_set_bytes(sh.K, sh.N, wl.G) for sh in wl.shapes)
         fl = sum(2.0 * M * sh.K * sh.N for sh in wl.shapes)
+        per_shape = {}
+        for sh in wl.shapes:
+            us = sum(t[sh.name]) / len(t[sh.name]) * 1e3
+            per_shape[sh.name] = {"avg_us": round(us, 2),
+                                  "weight_GBps": round(weight_set_bytes(sh.K, sh.N, wl.G) / us / 1e3, 1),
+                                  "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
+                                  "traffic": traffic_set_entry(f"{wl.name}/{sh.name}@M={M}")}
         out[f"M={M}"] = {"layer_us": round(layer_ms * 1e3, 2), "weight_GBps": round(wb / (layer_ms / 1e3) / 1e9, 1),
-                         "TFLOPs": round(fl / (layer_ms / 1e3) / 1e12, 2),
-                         "plans": {sh.name: awq.linear_plan(M, sh.K, sh.N, wl.G) for sh in wl.shapes}}
+                         "TFLOPs": round(fl / (layer_ms / 1e3) / 1e12, 2), "per_shape": per_shape}
         del stack
         torch.cuda.empty_cache()
     return out
@@ -920,6 +926,140 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, commands):
     print("\n".join(lines))
 
 
+def traffic_set_cases():
+    """The decode-path layers profiled by --traffic-set, in launch order:
+    the LLaMA-3-8B layer at every M of its sweep, one Falcon-180B-shaped
+    layer at M = 1 and 16, the Falcon-7B layer at group 64, M = 1 and 8.
+    Each: (label, K, N, G, M, scales, lo, hi)."""
+    import synth
+    cases = []
+    for wl in (synth.LLAMA3_8B_SWEEP, synth.FALCON_180B_STACK, synth.FALCON_7B_DECODE_G64):
+        for sh in wl.shapes:
+            for M in wl.Ms:
+                cases.append((f"{wl.name}/{sh.name}@M={M}", sh.K, sh.N, wl.G, M, wl.scales, wl.lo, wl.hi))
+    return cases
+
+
+TRAFFIC_SET_REPS = 3
+
+
+def run_traffic_set(awq, lib, torch, dev, seed):
+    """Launch every case of traffic_set_cases() TRAFFIC_SET_REPS times (automatic
+    plan), one case after another, for rocprofv3 counter and trace runs."""
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    ws = awq.Workspace(dev)
+    built = {}
+    for label, K, N, G, M, scales, lo, hi in traffic_set_cases():
+        key = (K, N, G, lo, hi)
+        if key not in built:
+            built.clear()
+            torch.cuda.empty_cache()
+            x = torch.randn((64, K), device=dev, generator=gen).half()
+            y = torch.empty((64, N), dtype=torch.float16, device=dev)
+            built[key] = Layer(awq, torch, K, N, G, gen, x[:1], y[:1], ws, dev, scales=(lo, hi))
+            built["x"], built["y"] = x, y
+        L = built[key].rebound(awq, built["x"][:M], built["y"][:M], ws)
+        for _ in range(TRAFFIC_SET_REPS):
+            L.launch(lib, stream)
+        torch.cuda.synchronize()
+        eprint(f"[bench] traffic set: {label} plan {awq.linear_plan(M, K, N, G)}")
+
+
+def summarize_traffic_set(trace_dir, fetch_dir, write_dir, commands):
+    """profiles/decode_sweep_falcon_g64_traffic.md and decode_set_traffic.json
+    from the CSV output of three rocprofv3 runs of `bench.py --traffic-set`
+    (kernel trace; --pmc FETCH_SIZE; --pmc WRITE_SIZE, the counter runs with
+    --copy-calibration). A call is a decode kernel and, for a plan that splits
+    K, the reduction kernel after it; calls come case by case in
+    traffic_set_cases() order, TRAFFIC_SET_REPS per case."""
+    import csv
+    import statistics
+
+    def rows(d, name):
+        with open(os.path.join(d, name)) as f:
+            return sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"]))
+
+    cases = traffic_set_cases()
+
+    def calls(rs):
+        out, last = [], None
+        for r in rs:
+            name = _short(r["Kernel_Name"])
+            if "decode_" in name:
+                last = [(name, r)]
+                out.append(last)
+            elif "prefill_reduce" in name and last is not None:
+                last.append((name, r))
+        if len(out) != len(cases) * TRAFFIC_SET_REPS:
+            raise RuntimeError(f"{len(out)} decode calls for {len(cases)} cases x {TRAFFIC_SET_REPS}")
+        return {c[0]: out[i * TRAFFIC_SET_REPS:(i + 1) * TRAFFIC_SET_REPS] for i, c in enumerate(cases)}
+
+    tr = calls(rows(trace_dir, "bench_kernel_trace.csv"))
+
+    def counters(d):
+        rs = rows(d, "bench_counter_collection.csv")
+        copy = [float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]]
+        return calls([r for r in rs if "awq::" in r["Kernel_Name"]]), copy[-1]
+
+    fe, copy_f = counters(fetch_dir)
+    wr, copy_w = counters(write_dir)
+    ff, fw = (1 << 30) / (copy_f * 1024), (1 << 30) / (copy_w * 1024)
+    lines = ["# rocprofv3 summary: decode-path kernels on the batched LLaMA-3-8B layer, a Falcon-180B-shaped layer "
+             "and the Falcon-7B layer at group 64, one MI355X", "",
+             "Layers (automatic plans): LLaMA-3-8B QKV 4096x6144, O 4096x4096, gate+up 4096x28672, down 14336x4096 "
+             "at M = 1, 2, 4, 8, 16, 32 (G = 128); Falcon-180B-shaped QKV 14848x15872, O 14848x14848, up "
+             "14848x59392, down 59392x14848 at M = 1 and 16 (G = 128); Falcon-7B QKV 4544x4672, O 4544x4544, up "
+             "4544x18176, down 18176x4544 at M = 1 and 8 (G = 64). Each layer is launched "
+             f"{TRAFFIC_SET_REPS} times in a row.", "", "Commands (each run from /tmp with TMPDIR=/tmp):", ""]
+    lines += [f"    {c}" for c in commands]
+    lines += ["", "The table comes from `python bench.py --summarize-traffic-set TRACE FETCH WRITE` on their output "
+              "directories.", "",
+              f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = {copy_f:.1f} KiB and WRITE_SIZE = "
+              f"{copy_w:.1f} KiB, so the per-call counters below are scaled by {ff:.4f} (fetch) and {fw:.4f} "
+              "(write). Algorithmic bytes = weight set + 2MK (x) + 2MN (y); a K split adds its fp32 partials "
+              "(written and read back, 8 split M N) to the traffic but not to the algorithmic bytes.", "",
+              "| layer | kernels of one call | kernel-trace us (median) | weight GB/s | FETCH_SIZE KiB | WRITE_SIZE KiB "
+              "| HBM bytes (scaled) | algorithmic bytes | ratio |",
+              "|---|---|---|---|---|---|---|---|---|"]
+    out = {}
+    for label, K, N, G, M, *_ in cases:
+        us = statistics.median(sum((float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) / 1e3 for _, r in c)
+                               for c in tr[label])
+        names = " + ".join(f"{n} (grid {r.get('Grid_Size_X') or r.get('Grid_Size')})" for n, r in tr[label][0])
+        fk = statistics.mean(sum(float(r["Counter_Value"]) for _, r in c) for c in fe[label])
+        wk = statistics.mean(sum(float(r["Counter_Value"]) for _, r in c) for c in wr[label])
+        hbm = fk * 1024 * ff + wk * 1024 * fw
+        wb = weight_set_bytes(K, N, G)
+        alg = wb + 2 * M * K + 2 * M * N
+        lines.append(f"| {label} | {names} | {us:.2f} | {wb / us / 1e3:.0f} | {fk:.0f} | {wk:.0f} | "
+                     f"{hbm / 1e6:.2f} MB | {alg / 1e6:.2f} MB | {hbm / alg:.3f} |")
+        out[label] = {"kernels": names, "median_us": round(us, 3), "hbm_bytes_per_launch": hbm,
+                      "alg_bytes_per_launch": alg}
+    md = os.path.join(ROOT, "profiles", "decode_sweep_falcon_g64_traffic.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", "decode_set_traffic.json"), "w") as f:
+        json.dump({"kernel_source_sha": source_sha(KERNEL_SOURCES["decode"]), "fetch_scale": ff,
+                   "write_scale": fw, "shapes": out, "source": os.path.basename(md)}, f, indent=1)
+    print(md)
+
+
+def traffic_set_entry(label):
+    """HBM bytes per call of a decode-set layer (profiles/decode_set_traffic.json),
+    if taken on the current decode kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "decode_set_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != source_sha(KERNEL_SOURCES["decode"]):
+        return None
+    entry = t.get("shapes", {}).get(label)
+    return round(entry["hbm_bytes_per_launch"]) if entry else None
+
+
 def traffic_entry(kernel, shape):
     """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the counters'
     reading of a plain copy of known size) from the committed rocprofv3
@@ -959,10 +1099,18 @@ def main():
                     help="the rocprofv3 command lines, quoted in the summary")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter calibration)")
+    ap.add_argument("--traffic-set", action="store_true",
+                    help="only launch the decode-path profiling set (batched LLaMA-3-8B, Falcon-180B and Falcon-7B "
+                         "group-64 layers) for rocprofv3, then exit")
+    ap.add_argument("--summarize-traffic-set", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries of --traffic-set runs, then exit")
     args = ap.parse_args()
 
     if args.summarize_profiles:
         summarize_profiles(*args.summarize_profiles, args.profile_commands)
+        return
+    if args.summarize_traffic_set:
+        summarize_traffic_set(*args.summarize_traffic_set, args.profile_commands)
         return
 
     if args.gpus != 1:
@@ -978,6 +1126,15 @@ def main():
     lib = awq.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.traffic_set:
+        run_traffic_set(awq, lib, torch, dev, args.seed + 9)
+        if args.copy_calibration:
+            a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+            b = torch.empty_like(a)
+            b.copy_(a)
+            torch.cuda.synchronize()
+            eprint("[bench] copy calibration: 1 GiB device copy done")
+        return
     hip = HipEvents()
     wl = synth.LLAMA2_7B_DECODE
     M = 1
