@@ -20,12 +20,21 @@
 //   * Scales and packed zero words of the workgroup's columns for the step's
 //     groups ride along the same way (one dword per thread each).
 //   * Weights: each wave reads the packed words of its own columns straight
-//     from global memory into registers one step ahead (KS/128 of the lane's
-//     16-byte slice of a 128-row tile per column tile) and decodes them right
-//     before their MFMA. Tiles of one 128-row band are adjacent in the device
-//     layout, so these reads are contiguous.
-//   * One barrier per step; out-of-range rows, columns and K read zero (the
-//     loads' out-of-range lanes write zeros to LDS) and are never stored.
+//     from global memory into registers (KS/128 of the lane's 16-byte slice
+//     of a 128-row tile per column tile); tiles of one 128-row band are
+//     adjacent in the device layout, so these reads are contiguous.
+//   * Software pipeline inside a step: iteration (substep, column tile)
+//     issues that tile's MFMAs for all of the wave's row tiles, decodes the
+//     next tile's words in between (about two VALU instructions per MFMA,
+//     which the matrix core's issue gaps absorb), and carries a share of
+//     the next stage's loads: activations, scales and zero points in the
+//     first substep, the next step's weight words 2-3 in the second and
+//     words 0-1 (into the registers of this step's, decoded by then) in the
+//     third. A row tile's A fragment for the next substep is read from LDS
+//     right after its last MFMA in this one.
+//   * One barrier per step; rows past M and K past the end read zero
+//     through the buffers' range checks; columns past N get zero scales, so
+//     their outputs are zero, and are never stored.
 //   * Split-K (for layers with fewer output tiles than the chip has
 //     workgroup slots): workgroup (split, tile) covers a contiguous range of
 //     K steps and writes fp32 partial sums to ws[split][M][N]; a second
@@ -143,16 +152,19 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
 
   // Activation load j of this thread fills slab chunk p = (j*NW + wave)*64 + lane:
   // row p / CPR, stored column p % CPR, i.e. global chunk (p % CPR) ^ (row % CPR).
-  uint32_t a_goff[C::A_DMA], a_k[C::A_DMA];
-#pragma unroll
-  for (int j = 0; j < C::A_DMA; ++j) {
-    const uint32_t p = (uint32_t)(j * C::NW + wv) * 64u + (uint32_t)lane;
-    const uint32_t row = p / C::CPR;
-    const uint32_t ch = (p % C::CPR) ^ (row % C::CPR);
-    const int grow = m0 + (int)row;
-    a_goff[j] = grow < M ? ((uint32_t)grow * (uint32_t)K + 8u * ch) * 2u : kOOB;
-    a_k[j] = 8u * ch;
+  // Consecutive loads are NW*64/CPR rows apart, a multiple of CPR, so the
+  // chunk (and the column a_k it starts at) is the same for every j.
+  static_assert((C::NW * 64 / C::CPR) % C::CPR == 0, "one swizzled chunk per thread");
+  // Rows past M lie past the end of x (M*K*2 < 2^31 bytes, so no offset
+  // wraps) and read zeros through the buffer's range check.
+  constexpr int A_ROWS = C::NW * 64 / C::CPR;  // rows between consecutive loads
+  uint32_t a_base, a_k;
+  {
+    const uint32_t p0 = (uint32_t)wv * 64u + (uint32_t)lane;
+    a_k = 8u * ((p0 % C::CPR) ^ ((p0 / C::CPR) % C::CPR));
+    a_base = ((uint32_t)(m0 + (int)(p0 / C::CPR)) * (uint32_t)K + a_k) * 2u;
   }
+  const uint32_t a_step = (uint32_t)A_ROWS * (uint32_t)K * 2u;
   // Dword tid of the scale region: columns 2c, 2c+1 of group row gi; of the
   // zero region: packed word c of group row gi.
   const int sc_gi = tid / (C::BN / 2), sc_col = gcol(2 * (tid % (C::BN / 2)));
@@ -165,48 +177,98 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   auto lcol = [&](int nt) {
     return EPI ? (nt < NTW / 2 ? 0 : C::BN / 2) + 16 * (NTW / 2) * wn + 16 * (nt % (NTW / 2)) : 16 * (NTW * wn + nt);
   };
-  // This lane's slice of each of the wave's NTW column tiles in band 0.
-  uint32_t b_off[NTW];
+  // This lane's slice of the wave's column tiles in band 0: the tiles of one
+  // half (all NTW plain, NTW/2 gate or up) are consecutive, 1 KiB apart.
+  // Tiles past the last column read whatever the buffer holds there (zero
+  // past its end); their outputs are never stored.
+  uint32_t b_off[EPI ? 2 : 1];
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int ct = gcol(lcol(nt)) / 16;
-    b_off[nt] = gvalid(lcol(nt)) ? (uint32_t)ct * 1024u + (uint32_t)lane * 16u : kOOB;
-  }
-
-  auto issue_stage = [&](int step, int buf) {
-    char* st = smem + buf * C::STAGE;
-    const uint32_t k0 = (uint32_t)step * KS;
-#pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j) {
-      const uint32_t bad = (uint32_t)!(k0 + a_k[j] < (uint32_t)K) << 31;
-      load_to_lds16(rx, st + (j * C::NW + wv) * 1024, (a_goff[j] + k0 * 2u) | bad);
-    }
-    const int g0 = GS > 1 ? step * GS : (step * KS) / G;  // first group of the step
-    const int sg = g0 + sc_gi, zg = g0 + zw_gi;
-    const uint32_t sbad = (uint32_t)!(sc_ok && sg < groups) << 31;
-    const uint32_t zbad = (uint32_t)!(zw_ok && zg < groups) << 31;
-    load_to_lds4(rs, st + C::SC_OFF + wv * 256, ((uint32_t)sg * (uint32_t)N + (uint32_t)sc_col) * 2u | sbad);
-    load_to_lds4(rz, st + C::ZW_OFF + wv * 256, ((uint32_t)zg * (uint32_t)(N / 8) + (uint32_t)zw_w) * 4u | zbad);
-  };
-  auto load_b = [&](int step, wvec(&rb)[NTW]) {
-    const uint32_t band = KS == 128 ? (uint32_t)step * (uint32_t)NT * 1024u
-                                    : (uint32_t)(step >> 1) * (uint32_t)NT * 1024u + (uint32_t)(step & 1) * 8u;
-#pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) rb[nt] = WW::load(rq, b_off[nt] + band);
-  };
-
+  for (int hh = 0; hh < (EPI ? 2 : 1); ++hh)
+    b_off[hh] = (uint32_t)(gcol(lcol(hh * (NTW / 2))) / 16) * 1024u + (uint32_t)lane * 16u;
   f4 acc[MTW][NTW];
 #pragma unroll
   for (int a = 0; a < MTW; ++a)
 #pragma unroll
     for (int b = 0; b < NTW; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
-  wvec cb[NTW], rb[NTW];
-  issue_stage(step0, 0);
-  load_b(step0, cb);
+  constexpr int KB = C::KB;
+  constexpr int NIT = KB * NTW;  // (substep, column tile) iterations per step
+  // KS = 128: the next step's weight words 2-3 of a column tile load into a
+  // register pair of their own (second substep) and words 0-1 into this
+  // step's once decoded (third substep); the other loads of the next stage
+  // go in the first substep. KS = 64: whole next-step words into a copy.
+  constexpr bool SPLITW = KB == 4;
+  constexpr int NLD = (SPLITW ? 0 : NTW) + C::A_DMA + 2;  // loads spread by issue_item
+  constexpr int NSLOT = SPLITW ? NTW : NIT;                  // iterations that carry them
 
-  const DecodeConsts kc = decode_consts();
+  DecodeConsts kc;
+  kc.m1 = 0x000F000Fu;
+  kc.m2 = 0x00F000F0u;
+  kc.o1 = 0x64006400u;
+  kc.o2 = 0x54005400u;
+  // masks in VGPRs, OR patterns in SGPRs: one v_and_or_b32 each
+  asm volatile("" : "+v"(kc.m1), "+v"(kc.m2), "+s"(kc.o1), "+s"(kc.o2));
+
   const int arow0 = 16 * MTW * wm + (lane & 15);
+  wvec cb[NTW], rb[SPLITW ? 1 : NTW];
+  u2 w23[SPLITW ? NTW : 1];
+  h8 af[MTW];
+  ZeroConst zc[NTW];
+  h2 s2[NTW];
+  // zero point and scale of column tile nt for group gi of a stage
+  auto zs_of = [&](const char* st, int gi, int nt) {
+    const uint16_t* sc_l = reinterpret_cast<const uint16_t*>(st + C::SC_OFF);
+    const uint32_t* zw_l = reinterpret_cast<const uint32_t*>(st + C::ZW_OFF);
+    const int c = lcol(nt) + (lane & 15);
+    const uint32_t zw = zw_l[gi * (C::BN / 8) + c / 8];
+    zc[nt] = zero_const((zw >> (4 * (c % 8))) & 0xFu);
+    s2[nt] = splat_h2(sc_l[gi * C::BN + c]);
+  };
+  auto grp = [](int s) { return GS == 1 ? 0 : s / (KB / GS); };
+  auto wband = [&](int step) {
+    return KS == 128 ? (uint32_t)step * (uint32_t)NT * 1024u
+                     : (uint32_t)(step >> 1) * (uint32_t)NT * 1024u + (uint32_t)(step & 1) * 8u;
+  };
+  auto woff = [&](int nt) {
+    return EPI ? b_off[nt / (NTW / 2)] + (uint32_t)(nt % (NTW / 2)) * 1024u : b_off[0] + (uint32_t)nt * 1024u;
+  };
+  // Load item i of the next stage: (KS = 64 only) weight tile i, then
+  // activation chunk j, then the scale and the zero-point dword. inv (bit
+  // 31) puts a load out of range: it reads zeros (past the last step).
+  auto issue_item = [&](int i, int step, int buf, uint32_t inv) {
+    if (SPLITW) i += NTW;
+    if (i < NTW) {
+      rb[SPLITW ? 0 : i] = WW::load(rq, (woff(i) + wband(step)) | inv);
+      return;
+    }
+    char* stn = smem + buf * C::STAGE;
+    const uint32_t k0 = (uint32_t)step * KS;
+    if (i < NTW + C::A_DMA) {
+      const int j = i - NTW;
+      const uint32_t bad = ((uint32_t)!(k0 + a_k < (uint32_t)K) << 31) | inv;
+      uint32_t a0 = a_base + k0 * 2u;
+      asm volatile("" : "+v"(a0));  // keeps the per-load offsets out of the loop's invariants
+      load_to_lds16(rx, stn + (j * C::NW + wv) * 1024, (a0 + (uint32_t)j * a_step) | bad);
+      return;
+    }
+    const int g0 = GS > 1 ? step * GS : (step * KS) / G;  // first group of the step
+    if (i == NTW + C::A_DMA) {
+      const int sg = g0 + sc_gi;
+      const uint32_t sbad = ((uint32_t)!(sc_ok && sg < groups) << 31) | inv;
+      load_to_lds4(rs, stn + C::SC_OFF + wv * 256, ((uint32_t)sg * (uint32_t)N + (uint32_t)sc_col) * 2u | sbad);
+    } else {
+      const int zg = g0 + zw_gi;
+      const uint32_t zbad = ((uint32_t)!(zw_ok && zg < groups) << 31) | inv;
+      load_to_lds4(rz, stn + C::ZW_OFF + wv * 256, ((uint32_t)zg * (uint32_t)(N / 8) + (uint32_t)zw_w) * 4u | zbad);
+    }
+  };
+
+  // Prologue: the first stage and its weights.
+#pragma unroll
+  for (int i = SPLITW ? 0 : NTW; i < NLD; ++i) issue_item(i, step0, 0, 0u);
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) cb[nt] = WW::load(rq, woff(nt) + wband(step0));
+
   for (int step = step0; step < step1; ++step) {
     // Wait for this wave's loads of the current stage, then for everyone's;
     // the barrier also frees the other buffer (read during the last step).
@@ -215,43 +277,70 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
     // of them), and an explicit s_waitcnt is never relaxed.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    const bool more = step + 1 < step1;
-    if (more) {
-      load_b(step + 1, rb);
-      issue_stage(step + 1, (step + 1 - step0) & 1);
-    }
+    const uint32_t inv = (uint32_t)!(step + 1 < step1) << 31;
+    const int nbuf = (step + 1 - step0) & 1;
     const char* st = smem + ((step - step0) & 1) * C::STAGE;
-    const uint16_t* sc_l = reinterpret_cast<const uint16_t*>(st + C::SC_OFF);
-    const uint32_t* zw_l = reinterpret_cast<const uint32_t*>(st + C::ZW_OFF);
-    ZeroConst zc[NTW];
-    h2 s2[NTW];
+    auto frag = [&](int s, int mt) -> h8 {
+      return *reinterpret_cast<const h8*>(st + swz<C::CPR>((uint32_t)(arow0 + 16 * mt), (uint32_t)(4 * s + h)));
+    };
 #pragma unroll
-    for (int s = 0; s < C::KB; ++s) {
-      const int gi = GS == 1 ? 0 : s / (C::KB / GS);
-      if (s == 0 || (GS > 1 && s % (C::KB / GS) == 0)) {
+    for (int nt = 0; nt < NTW; ++nt) zs_of(st, 0, nt);
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const int c = lcol(nt) + (lane & 15);
-          const uint32_t zw = zw_l[gi * (C::BN / 8) + c / 8];
-          zc[nt] = zero_const((zw >> (4 * (c % 8))) & 0xFu);
-          s2[nt] = splat_h2(sc_l[gi * C::BN + c]);
+    for (int mt = 0; mt < MTW; ++mt) af[mt] = frag(0, mt);
+    h8 bcur = decode_weight_vk(cb[0][0], zc[0], s2[0], kc), bnext;
+    if (GS > 1 && KB > 1 && grp(1) != grp(0)) zs_of(st, grp(1), 0);
+    // Iteration (s, nt): the 8 MFMAs of column tile nt in substep s, with
+    // the next tile's decode and a share of the next stage's loads between
+    // them. A scheduling fence ends each iteration: left free, the compiler
+    // hoists loads and decodes across iterations and runs out of registers.
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int s = it / NTW, nt = it % NTW;
+      // the next stage's loads; past the last step they read zeros, so the
+      // step has no branch
+      if (SPLITW) {
+        if (s == 0) {
+#pragma unroll
+          for (int i = (nt * NLD + NSLOT - 1) / NSLOT; i < ((nt + 1) * NLD + NSLOT - 1) / NSLOT; ++i)
+            issue_item(i, step + 1, nbuf, inv);
+        } else if (s == 1) {
+          w23[nt] = __builtin_bit_cast(
+              u2, __builtin_amdgcn_raw_buffer_load_b64(rq, (woff(nt) + wband(step + 1) + 8u) | inv, 0, 0));
+        } else if (s == 2) {
+          const u2 w01 = __builtin_bit_cast(
+              u2, __builtin_amdgcn_raw_buffer_load_b64(rq, (woff(nt) + wband(step + 1)) | inv, 0, 0));
+          cb[nt][0] = w01[0];
+          cb[nt][1] = w01[1];
         }
+      } else {
+#pragma unroll
+        for (int i = (it * NLD + NIT - 1) / NIT; i < ((it + 1) * NLD + NIT - 1) / NIT; ++i)
+          issue_item(i, step + 1, nbuf, inv);
       }
-      h8 af[MTW];
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-        af[mt] = *reinterpret_cast<const h8*>(st + swz<C::CPR>((uint32_t)(arow0 + 16 * mt), (uint32_t)(4 * s + h)));
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const h8 bw = decode_weight_vk(cb[nt][s], zc[nt], s2[nt], kc);
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bw, acc[mt][nt], 0, 0, 0);
+      // decode the next column tile while this one's MFMAs run; at a group
+      // boundary, that tile's zero point and scale for its next substep
+      if (it + 1 < NIT) {
+        const int s1 = (it + 1) / NTW, n1 = (it + 1) % NTW;
+        bnext = decode_weight_vk(cb[n1][s1], zc[n1], s2[n1], kc);
+        if (GS > 1 && s1 + 1 < KB && grp(s1 + 1) != grp(s1)) zs_of(st, grp(s1 + 1), n1);
       }
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt) {
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[mt], bcur, acc[mt][nt], 0, 0, 0);
+        // the next substep's fragment right after this one's last use
+        if (nt == NTW - 1 && s + 1 < KB) af[mt] = frag(s + 1, mt);
+      }
+      if (it + 1 < NIT) bcur = bnext;
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) {
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) cb[nt] = rb[nt];
+    for (int nt = 0; nt < NTW; ++nt) {
+      if (SPLITW) {
+        cb[nt][2] = w23[nt][0];
+        cb[nt][3] = w23[nt][1];
+      } else {
+        cb[nt] = rb[nt];
+      }
     }
   }
 
