@@ -26,12 +26,11 @@
 //   * Software pipeline inside a step: iteration (substep, column tile)
 //     issues that tile's MFMAs for all of the wave's row tiles, decodes the
 //     next tile's words in between (about two VALU instructions per MFMA,
-//     which the matrix core's issue gaps absorb), and carries a share of
-//     the next stage's loads: activations, scales and zero points in the
-//     first substep, the next step's weight words 2-3 in the second and
-//     words 0-1 (into the registers of this step's, decoded by then) in the
-//     third. A row tile's A fragment for the next substep is read from LDS
-//     right after its last MFMA in this one.
+//     which the matrix core's issue gaps absorb), and carries an even share
+//     of the next stage's loads (the next step's weight words first, into a
+//     second register set, then activations, scales and zero points). A row
+//     tile's A fragment for the next substep is read from LDS right after its
+//     last MFMA in this one.
 //   * One barrier per step; rows past M and K past the end read zero
 //     through the buffers' range checks; columns past N get zero scales, so
 //     their outputs are zero, and are never stored.
@@ -192,14 +191,8 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
     for (int b = 0; b < NTW; ++b) acc[a][b] = f4{0.f, 0.f, 0.f, 0.f};
 
   constexpr int KB = C::KB;
-  constexpr int NIT = KB * NTW;  // (substep, column tile) iterations per step
-  // KS = 128: the next step's weight words 2-3 of a column tile load into a
-  // register pair of their own (second substep) and words 0-1 into this
-  // step's once decoded (third substep); the other loads of the next stage
-  // go in the first substep. KS = 64: whole next-step words into a copy.
-  constexpr bool SPLITW = KB == 4;
-  constexpr int NLD = (SPLITW ? 0 : NTW) + C::A_DMA + 2;  // loads spread by issue_item
-  constexpr int NSLOT = SPLITW ? NTW : NIT;                  // iterations that carry them
+  constexpr int NIT = KB * NTW;            // (substep, column tile) iterations per step
+  constexpr int NLD = NTW + C::A_DMA + 2;  // next-stage loads, spread evenly over the iterations
 
   DecodeConsts kc;
   kc.m1 = 0x000F000Fu;
@@ -210,8 +203,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   asm volatile("" : "+v"(kc.m1), "+v"(kc.m2), "+s"(kc.o1), "+s"(kc.o2));
 
   const int arow0 = 16 * MTW * wm + (lane & 15);
-  wvec cb[NTW], rb[SPLITW ? 1 : NTW];
-  u2 w23[SPLITW ? NTW : 1];
+  wvec cb[NTW], rb[NTW];
   h8 af[MTW];
   ZeroConst zc[NTW];
   h2 s2[NTW];
@@ -232,13 +224,12 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
   auto woff = [&](int nt) {
     return EPI ? b_off[nt / (NTW / 2)] + (uint32_t)(nt % (NTW / 2)) * 1024u : b_off[0] + (uint32_t)nt * 1024u;
   };
-  // Load item i of the next stage: (KS = 64 only) weight tile i, then
+  // Load item i of the next stage: weight tile i (into the copy), then
   // activation chunk j, then the scale and the zero-point dword. inv (bit
   // 31) puts a load out of range: it reads zeros (past the last step).
   auto issue_item = [&](int i, int step, int buf, uint32_t inv) {
-    if (SPLITW) i += NTW;
     if (i < NTW) {
-      rb[SPLITW ? 0 : i] = WW::load(rq, (woff(i) + wband(step)) | inv);
+      rb[i] = WW::load(rq, (woff(i) + wband(step)) | inv);
       return;
     }
     char* stn = smem + buf * C::STAGE;
@@ -265,7 +256,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
 
   // Prologue: the first stage and its weights.
 #pragma unroll
-  for (int i = SPLITW ? 0 : NTW; i < NLD; ++i) issue_item(i, step0, 0, 0u);
+  for (int i = NTW; i < NLD; ++i) issue_item(i, step0, 0, 0u);
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) cb[nt] = WW::load(rq, woff(nt) + wband(step0));
 
@@ -296,27 +287,11 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
       const int s = it / NTW, nt = it % NTW;
-      // the next stage's loads; past the last step they read zeros, so the
-      // step has no branch
-      if (SPLITW) {
-        if (s == 0) {
+      // the next stage's loads, weights first; past the last step they read
+      // zeros, so the step has no branch
 #pragma unroll
-          for (int i = (nt * NLD + NSLOT - 1) / NSLOT; i < ((nt + 1) * NLD + NSLOT - 1) / NSLOT; ++i)
-            issue_item(i, step + 1, nbuf, inv);
-        } else if (s == 1) {
-          w23[nt] = __builtin_bit_cast(
-              u2, __builtin_amdgcn_raw_buffer_load_b64(rq, (woff(nt) + wband(step + 1) + 8u) | inv, 0, 0));
-        } else if (s == 2) {
-          const u2 w01 = __builtin_bit_cast(
-              u2, __builtin_amdgcn_raw_buffer_load_b64(rq, (woff(nt) + wband(step + 1)) | inv, 0, 0));
-          cb[nt][0] = w01[0];
-          cb[nt][1] = w01[1];
-        }
-      } else {
-#pragma unroll
-        for (int i = (it * NLD + NIT - 1) / NIT; i < ((it + 1) * NLD + NIT - 1) / NIT; ++i)
-          issue_item(i, step + 1, nbuf, inv);
-      }
+      for (int i = (it * NLD + NIT - 1) / NIT; i < ((it + 1) * NLD + NIT - 1) / NIT; ++i)
+        issue_item(i, step + 1, nbuf, inv);
       // decode the next column tile while this one's MFMAs run; at a group
       // boundary, that tile's zero point and scale for its next substep
       if (it + 1 < NIT) {
@@ -334,14 +309,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) {
-      if (SPLITW) {
-        cb[nt][2] = w23[nt][0];
-        cb[nt][3] = w23[nt][1];
-      } else {
-        cb[nt] = rb[nt];
-      }
-    }
+    for (int nt = 0; nt < NTW; ++nt) cb[nt] = rb[nt];
   }
 
   // Lane l, register r of tile (mt, nt): row 4(l/16) + r, column l%16.
