@@ -6,7 +6,10 @@
 // section "New Optimization of Context Stage") every weight is reused by many
 // rows, so the layer is a dense contraction bound by the matrix cores. Each
 // packed weight is decoded to its exact fp16 value (q - z) * s once per wave
-// that uses it and fed to v_mfma_f32_16x16x32_f16.
+// that uses it and fed to v_mfma_f32_16x16x32_f16. In the 256 x 256 tile
+// every wave owns two column tiles for all 256 rows, so each weight is
+// decoded once per workgroup (the vector-ALU work per MFMA is what limits
+// this kernel; the price is twice the activation reads from LDS).
 //
 // Structure (per workgroup: WM x WN waves, each wave MTW x NTW tiles of 16x16
 // outputs; K advances KS rows per step):
@@ -549,7 +552,7 @@ hipError_t launch_prefill(const LinearArgs& a, int tile, int splits, float* ws, 
   switch (tile) {
     case 1: return launch_prefill_k<2, 2, 4, 4, 64>(a, splits, ws, gated, L);   // 128 x 128, 4 waves of 64 x 64, 64-row steps
     case 2: return launch_prefill_k<2, 2, 4, 4, 128>(a, splits, ws, gated, L);  // 128 x 128, 4 waves of 64 x 64, 128-row steps
-    case 3: return launch_prefill_k<2, 4, 8, 4, 128>(a, splits, ws, gated, L);  // 256 x 256, 8 waves of 128 x 64, 128-row steps
+    case 3: return launch_prefill_k<1, 8, 16, 2, 128>(a, splits, ws, gated, L);  // 256 x 256, 8 waves of 256 x 32, 128-row steps
   }
   return hipErrorInvalidValue;
 }
