@@ -68,9 +68,10 @@ def test_noalloc_matches_linear_two_calls(awq):
 
 def test_noalloc_automatic_plan_fits_the_array(awq):
     import torch
-    # awq_linear's automatic plan for this layer splits K three ways (126 MB
-    # of partials); the no-alloc call lowers the split until they fit.
-    M, K, N, G = 2048, 5120, 5120, 128
+    # awq_linear's automatic plan for this layer (the LLaMA-2-13B down
+    # projection at 2048 rows) splits K three ways (126 MB of partials); the
+    # no-alloc call lowers the split until they fit.
+    M, K, N, G = 2048, 13824, 5120, 128
     auto = awq.linear_plan(M, K, N, G)
     assert awq.linear_workspace_bytes(M, K, N, G) > SCRATCH_BYTES
     log(f"noalloc automatic M={M} K={K} N={N} awq_linear plan={auto}")

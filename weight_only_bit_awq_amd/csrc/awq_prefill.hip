@@ -467,24 +467,31 @@ namespace {
 // the LLaMA-shaped layers (MI355X): the workgroups run in rounds of
 // `slots` (resident workgroups per chip), each round takes one workgroup's
 // K range, and the split-K partials cost a write and a read of fp32 per
-// output per split. Times in microseconds.
+// output per split (the partial stores plus the reduction kernel). For the
+// 256 x 256 tile the time of one K step depends on how many workgroups run
+// at once: with all 256 CUs busy the chip is held at its power limit and
+// its clock drops (to about 2.0 GHz), so a round that leaves CUs idle runs
+// each step faster (measured: about 2.5 us with 100 or fewer busy, 2.7-2.9
+// with 160, 3.45 with 256). Times in microseconds.
 double prefill_cost(int M, int K, int N, int tile, int splits, double step_scale) {
   const int bm = tile == 3 ? 256 : 128, bn = tile == 3 ? 256 : 128;
   const double tiles = (double)((M + bm - 1) / bm) * (double)((N + bn - 1) / bn);
   const int steps = prefill_steps(K, tile);
   const double wgs = tiles * splits;
-  double slots, t_step;  // t_step: one K step of one workgroup
+  const double wg_steps = std::ceil((double)steps / splits) * step_scale;
+  const double reduce = splits > 1 ? 1.1e-6 * splits * (double)M * (double)N : 0.0;
   if (tile == 3) {
-    slots = 256, t_step = 3.8;
-  } else if (tile == 2) {
+    auto t_step = [](double busy) { return busy <= 96 ? 2.5 : 2.5 + (std::min(busy, 256.0) - 96) * (0.95 / 160); };
+    const double full = std::floor(wgs / 256), rest = wgs - full * 256;
+    return wg_steps * (full * t_step(256) + (rest > 0 ? t_step(rest) : 0.0)) + reduce;
+  }
+  double slots, t_step;  // t_step: one K step of one workgroup
+  if (tile == 2) {
     slots = 512, t_step = wgs <= 256 ? 1.6 : 2.8;  // alone on its CU, or sharing it
   } else {
     slots = 768, t_step = 1.9;
   }
-  const double rounds = std::ceil(wgs / slots);
-  const double per_wg = std::ceil((double)steps / splits) * t_step * step_scale;
-  const double reduce = splits > 1 ? 1.4e-6 * splits * (double)M * (double)N : 0.0;
-  return rounds * per_wg + reduce;
+  return std::ceil(wgs / slots) * wg_steps * t_step + reduce;
 }
 
 int best_split(int M, int K, int N, int tile, double step_scale, double* cost) {
