@@ -322,9 +322,9 @@ int w4a8_plan(int64_t M, int64_t K, int64_t N, const awq_plan* plan, int* tile, 
   if (plan && (plan->path || plan->waves || plan->tpw || plan->x_stage)) return AWQ_ERR_PLAN;
   if (*tile == 1 || *tile < 0 || *tile > 3 || *splits < 0 || *splits > 16) return AWQ_ERR_PLAN;
   if (*splits > (int)(K / 128)) return AWQ_ERR_PLAN;
-  // measured: a W4A8 K step takes about 0.7 of an fp16 step (LLaMA-2-13B
-  // shapes); with that the model picks the measured best plan on all of them
-  awq::prefill_auto_plan((int)M, (int)K, (int)N, tile, splits, 0.7);
+  // the W4A8 form of the model picks the measured best plan on every
+  // LLaMA-2-13B shape at M = 512 and 2048
+  awq::prefill_auto_plan((int)M, (int)K, (int)N, tile, splits, awq::PrefillKind::kW4A8);
   return AWQ_OK;
 }
 

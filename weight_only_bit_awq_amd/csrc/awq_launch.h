@@ -72,10 +72,11 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
 // into that many contiguous ranges whose fp32 partials go to `ws`
 // (prefill_workspace_bytes) and are summed by a second kernel.
 int prefill_steps(int K, int tile);
-// Fills *tile and/or *splits where they are 0, from a cost model;
-// step_scale scales its K-step time (1 for the fp16 GEMM; the W4A8 GEMM's
-// steps take about 0.7 of that, which favours fewer K splits).
-void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, double step_scale = 1.0);
+// Fills *tile and/or *splits where they are 0, from a cost model of the
+// fp16 GEMM (kFp16) or of the W4A8 GEMM (kW4A8), whose K steps are shorter
+// and, unlike the fp16 GEMM's, no faster when part of the chip is idle.
+enum class PrefillKind { kFp16, kW4A8 };
+void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, PrefillKind kind = PrefillKind::kFp16);
 // Gated (y[M, N/2] = silu(gate) * up): the partials always go through the
 // workspace and the reduction applies the epilogue.
 size_t prefill_workspace_bytes(int M, int N, int splits, bool gated);

@@ -468,38 +468,44 @@ namespace {
 // `slots` (resident workgroups per chip), each round takes one workgroup's
 // K range, and the split-K partials cost a write and a read of fp32 per
 // output per split (the partial stores plus the reduction kernel). For the
-// 256 x 256 tile the time of one K step depends on how many workgroups run
-// at once: with all 256 CUs busy the chip is held at its power limit and
-// its clock drops (to about 2.0 GHz), so a round that leaves CUs idle runs
-// each step faster (measured: about 2.5 us with 100 or fewer busy, 2.7-2.9
-// with 160, 3.45 with 256). Times in microseconds.
-double prefill_cost(int M, int K, int N, int tile, int splits, double step_scale) {
+// fp16 GEMM's 256 x 256 tile the time of one K step depends on how many
+// workgroups run at once: with all 256 CUs busy the chip is held at its
+// power limit and its clock drops (to about 2.0 GHz), so a round that
+// leaves CUs idle runs each step faster (measured: about 2.5 us with 100 or
+// fewer busy, 2.7-2.9 with 160, 3.45 with 256). The W4A8 GEMM's steps take
+// about 0.7 of the flat fp16 figure and do not speed up on a partly idle
+// chip (2.75 us per step at 160 busy, as at 256). Times in microseconds.
+double prefill_cost(int M, int K, int N, int tile, int splits, PrefillKind kind) {
   const int bm = tile == 3 ? 256 : 128, bn = tile == 3 ? 256 : 128;
   const double tiles = (double)((M + bm - 1) / bm) * (double)((N + bn - 1) / bn);
   const int steps = prefill_steps(K, tile);
   const double wgs = tiles * splits;
-  const double wg_steps = std::ceil((double)steps / splits) * step_scale;
-  const double reduce = splits > 1 ? 1.1e-6 * splits * (double)M * (double)N : 0.0;
-  if (tile == 3) {
+  const double wg_steps = std::ceil((double)steps / splits);
+  if (tile == 3 && kind == PrefillKind::kFp16) {
     auto t_step = [](double busy) { return busy <= 96 ? 2.5 : 2.5 + (std::min(busy, 256.0) - 96) * (0.95 / 160); };
     const double full = std::floor(wgs / 256), rest = wgs - full * 256;
+    const double reduce = splits > 1 ? 1.1e-6 * splits * (double)M * (double)N : 0.0;
     return wg_steps * (full * t_step(256) + (rest > 0 ? t_step(rest) : 0.0)) + reduce;
   }
   double slots, t_step;  // t_step: one K step of one workgroup
-  if (tile == 2) {
+  if (tile == 3) {
+    slots = 256, t_step = 3.8;
+  } else if (tile == 2) {
     slots = 512, t_step = wgs <= 256 ? 1.6 : 2.8;  // alone on its CU, or sharing it
   } else {
     slots = 768, t_step = 1.9;
   }
+  if (kind == PrefillKind::kW4A8) t_step *= 0.7;
+  const double reduce = splits > 1 ? 1.4e-6 * splits * (double)M * (double)N : 0.0;
   return std::ceil(wgs / slots) * wg_steps * t_step + reduce;
 }
 
-int best_split(int M, int K, int N, int tile, double step_scale, double* cost) {
+int best_split(int M, int K, int N, int tile, PrefillKind kind, double* cost) {
   const int steps = prefill_steps(K, tile);
   int best = 1;
-  double bc = prefill_cost(M, K, N, tile, 1, step_scale);
+  double bc = prefill_cost(M, K, N, tile, 1, kind);
   for (int s = 2; s <= 8 && s * 4 <= steps; ++s) {
-    const double c = prefill_cost(M, K, N, tile, s, step_scale);
+    const double c = prefill_cost(M, K, N, tile, s, kind);
     if (c < bc) bc = c, best = s;
   }
   if (cost) *cost = bc;
@@ -508,18 +514,18 @@ int best_split(int M, int K, int N, int tile, double step_scale, double* cost) {
 
 }  // namespace
 
-void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, double step_scale) {
+void prefill_auto_plan(int M, int K, int N, int* tile, int* splits, PrefillKind kind) {
   // A fixed tile gets its best split; a fixed split its best tile; else both.
   if (*tile && !*splits) {
-    *splits = best_split(M, K, N, *tile, step_scale, nullptr);
+    *splits = best_split(M, K, N, *tile, kind, nullptr);
     return;
   }
   double bc = 0;
   int bt = 0, bs = 1;
   for (int t = 2; t <= 3; ++t) {
     double c;
-    int s = *splits ? *splits : best_split(M, K, N, t, step_scale, &c);
-    if (*splits) c = prefill_cost(M, K, N, t, s, step_scale);
+    int s = *splits ? *splits : best_split(M, K, N, t, kind, &c);
+    if (*splits) c = prefill_cost(M, K, N, t, s, kind);
     if (!bt || c < bc) bc = c, bt = t, bs = s;
   }
   if (!*tile) *tile = bt;
