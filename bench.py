@@ -312,21 +312,27 @@ def gated_times(awq, lib, torch, hip, K, N, G, M, dev, copies, reps):
     nb = awq.linear_silu_mul_workspace_bytes(M, K, N, G)
     buf = ws.get(max(nb, awq.linear_workspace_bytes(M, K, N, G)))
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-    evs = hip.create(2 * reps * copies)
+    # The fused and the plain call alternate, layer by layer, so that both
+    # run in the same thermal and power state of the chip (timed one after
+    # the other, the same kernels differed by up to 8%); the first pass is
+    # untimed (it loads the kernels' code).
+    evs = hip.create(4 * reps * copies)
     fused, lin, elt = [], [], []
     for r in range(reps + 1):
         for i, L in enumerate(layers):
-            e = 2 * ((r % reps) * copies + i)
+            e = 4 * ((r % reps) * copies + i)
             st = lib.awq_linear_silu_mul_ex(x.data_ptr(), L.qw.data_ptr(), L.s.data_ptr(), L.zw.data_ptr(), M, K, N,
                                             G, yg.data_ptr(), buf.data_ptr() if buf is not None else None,
                                             buf.numel() if buf is not None else 0, None, stream, evs[e], evs[e + 1])
             if st:
                 raise RuntimeError(lib.awq_status_string(st).decode())
+            L.launch_timed(lib, stream, evs[e + 2], evs[e + 3])
         torch.cuda.synchronize()
         if r:
-            fused += [hip.elapsed_ms(evs[2 * ((r % reps) * copies + i)], evs[2 * ((r % reps) * copies + i) + 1])
-                      for i in range(copies)]
-    lin = per_kernel_times(lib, torch, hip, [("l", L) for L in layers], reps)["l"]
+            for i in range(copies):
+                e = 4 * ((r % reps) * copies + i)
+                fused.append(hip.elapsed_ms(evs[e], evs[e + 1]))
+                lin.append(hip.elapsed_ms(evs[e + 2], evs[e + 3]))
     # torch's silu and multiply captured in a graph and replayed, so that the
     # host's launch latency stays out of the per-call time
     side = torch.cuda.Stream()

@@ -187,8 +187,13 @@ def test_batched_decode_plans(lib):
     for K, N in [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]:
         p1 = awq.linear_plan(1, K, N, 128)
         assert p1["path"] == 1 and p1["x_stage"] == 1          # one row: staged activations
-    p = awq.linear_plan(8, 4096, 6144, 128)                     # 384 tiles: streamed, two tiles per workgroup
+    p = awq.linear_plan(8, 4096, 6144, 128)                     # 384 tiles: streamed, two tiles, eight waves
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 2, 8)
+    p = awq.linear_plan(16, 4096, 6144, 128)                    # from 16 rows: four waves
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 2, 4)
+    p = awq.linear_plan(8, 4096, 4096, 128)                     # 256 tiles, 8 rows: streamed, one tile
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 1, 4)
+    assert awq.linear_plan(4, 4096, 4096, 128)["x_stage"] == 1  # 4 rows: staged
     p = awq.linear_plan(32, 4096, 28672, 128)                   # 1792 tiles: four per workgroup
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 4, 4)
     p = awq.linear_plan(32, 4096, 28672, 32)                    # 32-row groups at 32 rows: two
@@ -198,7 +203,8 @@ def test_batched_decode_plans(lib):
     p = awq.linear_plan(32, 14336, 4096, 128)                   # long K, narrow, 32 rows: K split four ways
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (1, 2, 4, 8, 4)
     assert awq.linear_workspace_bytes(32, 14336, 4096, 128) == 4 * 32 * 4096 * 4
-    assert awq.linear_plan(16, 14336, 4096, 128)["split_k"] == 1
+    assert awq.linear_plan(16, 14336, 4096, 128)["split_k"] == 4
+    assert awq.linear_plan(8, 14336, 4096, 128)["split_k"] == 1
     assert awq.linear_plan(32, 4096, 4096, 128)["split_k"] == 1
     assert awq.linear_plan(48, 4096, 28672, 128)["path"] == 2   # wide layer above 32 rows: GEMM
     assert awq.linear_plan(48, 4096, 4096, 128)["path"] == 1

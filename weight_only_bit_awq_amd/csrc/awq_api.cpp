@@ -152,18 +152,21 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
     int auto_split = 1;
-    if (!p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 24 && M <= 32 && NT <= 512 && KT >= 64) {
+    if (!p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 16 && M <= 32 && NT <= 512 && KT >= 64) {
       // Many rows on a narrow layer with a long K (e.g. the LLaMA-3-8B down
-      // projection, 14336 x 4096, at M = 32): four K ranges over workgroups
-      // of eight waves and four tiles, partials added by the reduction
-      // kernel (measured 29.7 -> 19.6 us; at M <= 16 or on shorter K the
-      // second launch costs more than it saves).
+      // projection, 14336 x 4096, at M = 16 .. 32): four K ranges over
+      // workgroups of eight waves and four tiles, partials added by the
+      // reduction kernel (measured 29.7 -> 19.6 us at M = 32, 16.8 -> 15.4
+      // at M = 16; at M <= 8 or on shorter K the second launch costs more
+      // than it saves).
       x_stage = 2, waves = 8, auto_split = 4;
-    } else if (!p.x_stage && M >= 4 && M <= 32 && NT >= 384) {
-      // Batched rows on layers of 384 or more tiles: the streamed variant,
-      // with adjacent tiles sharing each band's activation loads, beats
-      // staging the activations per workgroup (measured on the LLaMA-3-8B
-      // layers, M = 4 .. 32: e.g. QKV at M = 8, 5.9 against 11.6 us).
+    } else if (!p.x_stage && M >= 4 && M <= 32 && (NT >= 384 || M >= 8)) {
+      // Batched rows on layers of 384 or more tiles, and from 8 rows on
+      // narrower ones: the streamed variant, with adjacent tiles sharing
+      // each band's activation loads, beats staging the activations per
+      // workgroup (measured on the LLaMA-3-8B layers, M = 4 .. 32: e.g. QKV
+      // at M = 8, 5.9 against 11.6 us; O at M = 8, 5.6 against 6.5 with 16
+      // staging waves; O at M = 4 stays staged, 4.6 against 5.2).
       x_stage = 2;
       if (!p.waves) waves = 4;
     } else if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw)) {
@@ -195,6 +198,10 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
                   : (NT >= 896 && (M <= 16 || G >= 64))         ? 4
                   : NT >= 384                                   ? 2
                                                                 : 1;
+      // two tiles per workgroup at up to 8 rows: eight waves (LLaMA-3-8B
+      // QKV, 384 tiles: 5.7 against 6.3 us at M = 4, 6.0 against 6.3 at
+      // M = 8; four waves from 16 rows, and with four tiles)
+      if (!p.waves && auto_split == 1 && tpw == 2 && M <= 8) waves = 8;
     }
     if (p.tile) return AWQ_ERR_PLAN;
     out->waves = waves;
