@@ -119,8 +119,12 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     if (p.tpw > 4 || p.tpw == 3) return AWQ_ERR_PLAN;
     // Automatic choice (measured on the LLaMA-shaped decode layers, M = 1):
     // one 16-column tile per workgroup and eight waves splitting K, unless
-    // that makes more than about 12k waves (very wide layers: four), or the
-    // layer has fewer than 8 full 128-row bands.
+    // the layer has fewer than 8 full 128-row bands or is so wide that the
+    // workgroups need more than one round of the chip's wave slots: four
+    // waves above 8192 waves at G = 128 (the kernel is held to 64 VGPRs,
+    // 32 waves per CU; LLaMA-2-7B gate+up, 1376 tiles: 10.6-10.7 against
+    // 11.2 us), above about 12k at other group sizes (Falcon-7B up at
+    // G = 64, 1136 tiles: eight waves 13.3 against 13.6 us).
     if (gated) {
       // Fused gate+up: the staged kernel (halves of its waves on the gate
       // and the up tile) for one or two rows, else the streamed one with the
@@ -147,7 +151,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       return AWQ_OK;
     }
     int waves = p.waves;
-    if (!waves) waves = (NT * 8 > 12288 || KT < 8) ? 4 : 8;
+    if (!waves) waves = (NT * 8 > (G == 128 ? 8192 : 12288) || KT < 8) ? 4 : 8;
     int tpw = p.tpw;
     if (!tpw) tpw = 1;
     int x_stage = p.x_stage;
