@@ -176,13 +176,16 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     } else if (!p.waves && !p.x_stage && M >= 1 && !awq::decode_staged_fits((int)M, (int)K, G, waves, tpw)) {
       // Activations too large to stage with these waves: sixteen waves
       // stage twice as much per pass, but a 1024-thread workgroup with that
-      // much LDS holds a whole CU, so only where there are few workgroups (or
-      // one activation row, the long-K layers of Falcon-180B); otherwise the
-      // streamed variant with four waves.
-      if ((M <= 2 || NT <= 256) && awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
+      // much LDS holds a whole CU, so only where there are few workgroups;
+      // otherwise the streamed variant, with eight waves for one or two rows
+      // (the Falcon-180B-shaped down projection, 59392 x 14848 at M = 1:
+      // 84.9 us streamed with eight waves and four tiles per workgroup,
+      // against 92.8 staged with sixteen waves and 106.8 streamed with four)
+      // and four for more.
+      if (NT <= 256 && awq::decode_staged_fits((int)M, (int)K, G, 16, tpw))
         waves = 16;
       else
-        waves = 4;
+        waves = M <= 2 ? 8 : 4;
     }
     const bool fits = M >= 1 && p.tpw <= 2 && awq::decode_staged_fits((int)M, (int)K, G, waves, tpw);
     if (x_stage == 0) x_stage = fits ? 1 : 2;
