@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * WM * WN) void prefill_kernel(const uint16_t* _
     for (int mt = 0; mt < MTW; ++mt) af[mt] = frag(0, mt);
     h8 bcur = decode_weight_vk(cb[0][0], zc[0], s2[0], kc), bnext;
     if (GS > 1 && KB > 1 && grp(1) != grp(0)) zs_of(st, grp(1), 0);
-    // Iteration (s, nt): the 8 MFMAs of column tile nt in substep s, with
+    // Iteration (s, nt): the MTW MFMAs of column tile nt in substep s, with
     // the next tile's decode and a share of the next stage's loads between
     // them. A scheduling fence ends each iteration: left free, the compiler
     // hoists loads and decodes across iterations and runs out of registers.
