@@ -23,8 +23,11 @@
 //
 // The quotient w / s is formed as w * (1/s) and rounded; only when that
 // product lies within 2^-16 of a half-integer (where the two could round
-// differently) is the exact quotient taken, so the codes equal those of the
-// plain division for every input.
+// differently) is the exact quotient needed. The test is made once per device
+// word (eight rows of one column): if any of its eight products is that
+// close, the whole word is recomputed from exact quotients, so the codes
+// equal those of the plain division for every input and the common path has
+// no branch per weight.
 #include "awq_device.h"
 #include "awq_launch.h"
 
@@ -32,14 +35,31 @@ namespace awq {
 
 constexpr int kQuantCols = 64;
 
-// rne(w / s), from the product w * (1/s): the two differ by a few units in
-// the last place, so they can round differently only when the product lies
-// next to a half-integer; there the exact quotient is taken.
-__device__ __forceinline__ float rtn_quotient_rounded(float w, float s, float inv) {
-  const float t = w * inv;
-  const float r = rintf(t);
-  if (fabsf(t - r) > 0.5f - 1.52587890625e-05f) return rintf(w / s);
-  return r;
+// The device word of eight consecutive rows of one column: codes
+// clamp(rne(w / s) + z, 0, 15), row e in nibble 4(e % 2) + e / 2. The
+// quotients come from w * (1/s), which differs from w / s by a few units in
+// the last place, so the two can round differently only when the product
+// lies next to a half-integer; if any of the eight does, all eight are taken
+// from the exact quotient (one branch per word, rarely taken).
+__device__ __forceinline__ uint32_t rtn_word(const float (&f)[8], float s, float inv, float zf) {
+  float r[8], d = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float t = f[e] * inv;
+    r[e] = rintf(t);
+    d = fmaxf(d, fabsf(t - r[e]));
+  }
+  if (d > 0.5f - 1.52587890625e-05f) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = rintf(f[e] / s);
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float q = fminf(fmaxf(r[e] + zf, 0.f), 15.f);
+    word |= (uint32_t)q << (4 * (4 * (e & 1) + (e >> 1)));
+  }
+  return word;
 }
 
 // Scale (as float), its reciprocal and the zero point of one (group, column)
@@ -136,12 +156,10 @@ __global__ __launch_bounds__(256) void quantize_band_kernel(const uint16_t* __re
       const int c = 8 * co + i;
       uint32_t word = 0;
       if (ok) {
-        const float sf = p_s[gi][c], inv = p_inv[gi][c], zf = p_z[gi][c];
+        float f[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float q = fminf(fmaxf(rtn_quotient_rounded(half_at(v[e], i), sf, inv) + zf, 0.f), 15.f);
-          word |= (uint32_t)q << (4 * (4 * (e & 1) + (e >> 1)));
-        }
+        for (int e = 0; e < 8; ++e) f[e] = half_at(v[e], i);
+        word = rtn_word(f, p_s[gi][c], p_inv[gi][c], p_z[gi][c]);
       }
       const int cc = 8 * (co & 1) + i;
       tiles[tt][4 * (16 * h + cc) + j] = word;
@@ -233,15 +251,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const int n = n0 + c;
     if (n >= N) continue;
     const int k0 = g * G + 8 * (u / kQuantCols);
-    const float sf = col_s[c], inv = col_inv[c], zf = col_z[c];
     const uint16_t* src = w + (int64_t)k0 * N + n;
-    uint32_t word = 0;
+    float f[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = (float)__builtin_bit_cast(_Float16, src[(int64_t)e * N]);
-      const float q = fminf(fmaxf(rtn_quotient_rounded(f, sf, inv) + zf, 0.f), 15.f);
-      word |= (uint32_t)q << (4 * (4 * (e & 1) + (e >> 1)));
-    }
+    for (int e = 0; e < 8; ++e) f[e] = (float)__builtin_bit_cast(_Float16, src[(int64_t)e * N]);
+    const uint32_t word = rtn_word(f, col_s[c], col_inv[c], col_z[c]);
     const int kt = k0 / 128, j = (k0 % 128) / 32, h = (k0 % 32) / 8;
     qw[((int64_t)kt * NT + n / 16) * 256 + 4 * (16 * h + (n % 16)) + j] = word;
   }
