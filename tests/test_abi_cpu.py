@@ -181,12 +181,38 @@ def test_plans(lib):
     assert awq.linear_plan(512, 256, 5120, 128, {"path": 2, "tile": 2, "split_k": 8})["split_k"] == 2
 
 
+def test_prefill_plans_measured_choices(lib):
+    # the automatic prefill plans measured best on the LLaMA-2-13B layers
+    # (host logic only): the fp16 GEMM's step time depends on how many CUs
+    # are busy, so the 5120 x 5120 layer at M = 2048 (160 tiles) runs unsplit
+    # and the down projection (K = 13824) in three ranges; the W4A8 GEMM keeps
+    # its flat model (tile 2, three splits for the 5120 x 5120 layer at 512)
+    import weight_only_bit_awq_amd as awq
+    want = {(2048, 5120, 15360): 1, (2048, 5120, 5120): 1, (2048, 5120, 27648): 1, (2048, 13824, 5120): 3,
+            (512, 5120, 15360): 2, (512, 5120, 27648): 1, (512, 13824, 5120): 6}
+    for (M, K, N), split in want.items():
+        p = awq.linear_plan(M, K, N, 128)
+        assert (p["path"], p["tile"], p["split_k"]) == (2, 3, split), (M, K, N, p)
+    assert awq.linear_plan(512, 5120, 5120, 128)["split_k"] in (5, 6)
+    assert awq.linear_w4a8_plan(512, 5120, 5120, 128) == {"path": 2, "split_k": 3, "tile": 2}
+    assert awq.linear_w4a8_plan(2048, 5120, 5120, 128)["split_k"] == 1
+    assert awq.linear_w4a8_plan(2048, 13824, 5120, 128)["split_k"] == 3
+
+
 def test_batched_decode_plans(lib):
     # the automatic choices measured on the LLaMA-3-8B layers (host logic only)
     import weight_only_bit_awq_amd as awq
     for K, N in [(4096, 6144), (4096, 4096), (4096, 28672), (14336, 4096)]:
         p1 = awq.linear_plan(1, K, N, 128)
         assert p1["path"] == 1 and p1["x_stage"] == 1          # one row: staged activations
+    # eight-wave workgroups that would need more than one round of wave slots: four
+    assert awq.linear_plan(1, 4096, 22016, 128)["waves"] == 4   # 1376 tiles
+    assert awq.linear_plan(1, 4096, 16384, 128)["waves"] == 8   # 1024 tiles: one round
+    assert awq.linear_plan(1, 4544, 18176, 64)["waves"] == 8    # other group sizes: from ~1536 tiles
+    # one row whose activations need sixteen staging waves, on a wide layer: streamed, eight waves
+    p = awq.linear_plan(1, 59392, 14848, 128)
+    assert (p["x_stage"], p["waves"], p["tpw"]) == (2, 8, 4)
+    assert awq.linear_plan(1, 59392, 4096, 128)["waves"] == 16  # 256 tiles: staged with sixteen
     p = awq.linear_plan(8, 4096, 6144, 128)                     # 384 tiles: streamed, two tiles, eight waves
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 2, 8)
     p = awq.linear_plan(16, 4096, 6144, 128)                    # from 16 rows: four waves
