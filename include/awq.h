@@ -143,12 +143,13 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
  *            the decode path) computed by separate workgroups; their fp32
  *            partial sums go to the workspace and a second kernel adds them
  *            in a fixed order and rounds once to fp16 (results do not depend
- *            on scheduling). Prefill path: chosen automatically when the
- *            output has fewer tiles than the chip has workgroup slots (e.g.
- *            512 x 5120 outputs). Decode path: streamed variant only
- *            (x_stage 2); chosen automatically only for 24..32 rows on
- *            narrow layers with a long K, since the second launch costs
- *            more than the extra parallelism gains elsewhere.
+ *            on scheduling). Prefill path: chosen automatically from a
+ *            measured cost model when the output has fewer tiles than the
+ *            chip has workgroup slots and the split saves more than its
+ *            partials cost (e.g. 512 x 5120 outputs). Decode path: streamed
+ *            variant only (x_stage 2); chosen automatically only for 16..32
+ *            rows on narrow layers with a long K, since the second launch
+ *            costs more than the extra parallelism gains elsewhere.
  *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
  *            the K range of the workgroup's 16 columns and their partial sums
  *            are added through LDS in a fixed order.
