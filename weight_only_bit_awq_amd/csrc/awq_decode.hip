@@ -615,6 +615,13 @@ hipError_t launch_staged_s(const LinearArgs& a, const StagedSizes& z, const Laun
     if (per_wave == 5)
       return launch_staged_k<TM, WAVES>(decode_staged_kernel<TM, GPT, WAVES, 5, S>, a, z, L);
   }
+  // Twelve or more bands per wave at two groups per band (G = 64): six in
+  // flight (the Falcon-7B down projection, 18176 x 4544, 18 bands per wave:
+  // 16.0-16.4 against 16.5-17.0 us with four; nine gain nothing).
+  if constexpr (TM == 1 && GPT == 2) {
+    if (per_wave >= 12)
+      return launch_staged_k<TM, WAVES>(decode_staged_kernel<TM, GPT, WAVES, 6, S>, a, z, L);
+  }
   // the 64-VGPR build only where it compiles without spills: one group per
   // band, at most two 16-byte staging loads per thread, four or more waves
   if constexpr (TM != 2 && GPT == 1 && S <= 2 && WAVES >= 4)
