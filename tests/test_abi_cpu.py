@@ -279,6 +279,18 @@ def test_stream_read_validates_before_launch(lib):
     assert lib.awq_stream_read(ctypes.c_void_p(4104), 1024, ctypes.c_void_p(4096), None, None, None) == -4
 
 
+def test_w4a8_validates_before_launch(lib):
+    # an empty contraction (K = 0) writes y = 0: y is checked before that
+    # fill is enqueued; empty outputs touch no pointer
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.awq_linear_w4a8(None, None, None, None, 1, 0, 16, 128, None, None, 0, None) == -1
+    assert lib.awq_linear_w4a8(None, None, None, None, 1, 0, 16, 128, ctypes.c_void_p(0x1008), None, 0, None) == -4
+    assert lib.awq_linear_w4a8(None, None, None, None, 0, 0, 16, 128, None, None, 0, None) == 0
+    assert lib.awq_linear_w4a8(fake, fake, fake, fake, 1, 128, 16, 128, None, None, 0, None) == -1
+    assert lib.awq_linear_w4a8(fake, fake, fake, fake, 1, 100, 16, 128, fake, None, 0, None) == -2
+    assert lib.awq_linear_w4a8(fake, fake, fake, fake, 1, 128, 16, 128, fake, None, 0, None) == -5
+
+
 def _desc(**kw):
     import weight_only_bit_awq_amd as awq
     args = dict(B=1, q_heads=32, kv_heads=8, head_dim=128, capacity=4096, max_cached=4095)

@@ -348,8 +348,11 @@ int w4a8_run(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
   int st = w4a8_check(M, K, N, group);
   if (st) return st;
   if (M == 0 || N == 0) return AWQ_OK;
+  if (!y) return AWQ_ERR_NULL;
+  if (!aligned(y, 16)) return AWQ_ERR_ALIGN;
+  // empty contraction: y = 0, nothing else is read
   if (K == 0) return hip_status(awq::launch_fill_zero(y, M * N, L.stream));
-  if (!x || !qweight || !scales || !zeros || !y) return AWQ_ERR_NULL;
+  if (!x || !qweight || !scales || !zeros) return AWQ_ERR_NULL;
   if (!aligned(x, 16) || !aligned(qweight, 16) || !aligned(y, 16) || !aligned(scales, 4) || !aligned(zeros, 4))
     return AWQ_ERR_ALIGN;
   int tile, splits;
