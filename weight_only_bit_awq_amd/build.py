@@ -36,6 +36,18 @@ DEVICE_FLAGS = [
     # code object v5: loadable by the HIP runtime PyTorch ships as well as ROCm 7.2's
     "-mcode-object-version=5",
 ]
+# Per-source device flags. The decode kernels keep their MFMA results in
+# ordinary VGPRs instead of accumulation registers: the per-group scale is
+# applied to every group's result right after its MFMAs, so accumulation
+# registers only add a move per result register (four per 128-row band and
+# column tile) and registers (the staged kernel with four waves, as run on
+# the one-row gate+up layer: 72 -> 66; the streamed kernel for 16 and 32
+# rows with four tiles: 160 -> 138 and 244 -> 190). The instructions are
+# otherwise the same, and so are the results, bit for bit. The prefill GEMMs
+# hold 256x256 fp32 accumulator tiles and need the accumulation registers.
+SOURCE_FLAGS = {
+    "awq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc() -> str:
@@ -49,7 +61,7 @@ def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc()] + COMMON_FLAGS
     if src.endswith(".hip"):
-        cmd += DEVICE_FLAGS + ["-x", "hip"]
+        cmd += DEVICE_FLAGS + SOURCE_FLAGS.get(src, []) + ["-x", "hip"]
     else:
         cmd += ["-D__HIP_PLATFORM_AMD__"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
