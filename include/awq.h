@@ -147,19 +147,26 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
  *            measured cost model when the output has fewer tiles than the
  *            chip has workgroup slots and the split saves more than its
  *            partials cost (e.g. 512 x 5120 outputs). Decode path: streamed
- *            variant only (x_stage 2); chosen automatically only for 16..32
- *            rows on narrow layers with a long K, since the second launch
- *            costs more than the extra parallelism gains elsewhere.
- *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); they split
- *            the K range of the workgroup's 16 columns and their partial sums
- *            are added through LDS in a fixed order.
+ *            and slab variants only (x_stage 2, 3); chosen automatically for
+ *            16..32 rows on narrow layers with a long K and with the slab
+ *            variant, elsewhere the second launch costs more than the extra
+ *            parallelism gains.
+ *   waves:   decode path: waves per workgroup (1, 2, 4, 8 or 16); with
+ *            x_stage 1 or 2 they split the K range of the workgroup's columns
+ *            and their partial sums are added through LDS in a fixed order;
+ *            the slab variant runs 8 waves, each on its own columns.
  *   tpw:     decode path: 16-column tiles per workgroup: 1 or 2 with staged
  *            activations; 1, 2 or 4 with streamed activations (M <= 32, 4 or
- *            8 waves), where each wave's activation loads serve all of them.
+ *            8 waves), where each wave's activation loads serve all of them;
+ *            slab variant: tiles per wave, 2 or 4.
  *   x_stage: decode path: 1 = activations and the (scale, zero point) words
  *            of the workgroup's columns staged in LDS once per workgroup
  *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,
- *            scales and zero points read per tile.
+ *            scales and zero points read per tile, 3 = slab: the workgroup's
+ *            eight waves walk the same 128-row bands, the activations of two
+ *            bands at a time staged in LDS once for all of them (M <= 32, G a
+ *            multiple of 128; chosen automatically for 16..32 rows on the
+ *            largest layers and, above 16 rows, on wide ones).
  *   tile:    prefill path: workgroup tile 1 = 128x128 outputs (4 waves,
  *            64-row K steps, smallest LDS), 2 = 128x128 (4 waves, 128-row
  *            steps), 3 = 256x256 (8 waves, 128-row steps).

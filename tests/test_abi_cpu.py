@@ -220,8 +220,10 @@ def test_batched_decode_plans(lib):
     p = awq.linear_plan(8, 4096, 4096, 128)                     # 256 tiles, 8 rows: streamed, one tile
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 1, 4)
     assert awq.linear_plan(4, 4096, 4096, 128)["x_stage"] == 1  # 4 rows: staged
-    p = awq.linear_plan(32, 4096, 28672, 128)                   # 1792 tiles: four per workgroup
+    p = awq.linear_plan(16, 4096, 28672, 128)                   # 1792 tiles: four per workgroup
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 4, 4)
+    p = awq.linear_plan(32, 4096, 28672, 128)                   # above 16 rows, wide: slab, K in two
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (1, 3, 2, 8, 2)
     p = awq.linear_plan(32, 4096, 28672, 32)                    # 32-row groups at 32 rows: two
     assert p["tpw"] == 2
     p = awq.linear_plan(4, 14336, 4096, 128)                    # 256 tiles: staged, sixteen waves
@@ -238,6 +240,41 @@ def test_batched_decode_plans(lib):
         awq.linear_plan(1, 4096, 4096, 128, {"path": 1, "tpw": 4, "x_stage": 1})
     with pytest.raises(awq.AWQError):                           # and at most 32 rows
         awq.linear_plan(40, 4096, 4096, 128, {"path": 1, "tpw": 2, "x_stage": 2})
+
+
+def test_slab_plans(lib):
+    # x_stage 3 (eight waves on the same bands, two-band activation slabs in
+    # LDS): automatic on the largest 16-row layers and wide ones above 16
+    # rows, K split to about one round of workgroups with >= 16 bands each
+    import weight_only_bit_awq_amd as awq
+    p = awq.linear_plan(16, 14848, 59392, 128)                  # Falcon-180B-shaped up
+    assert (p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (3, 2, 8, 2)
+    p = awq.linear_plan(16, 59392, 14848, 128)                  # and down: 58 groups, 464 bands
+    assert (p["x_stage"], p["split_k"]) == (3, 8)
+    assert awq.linear_workspace_bytes(16, 59392, 14848, 128) == 8 * 16 * 14848 * 4
+    assert awq.linear_plan(16, 14848, 15872, 128)["x_stage"] == 2   # its QKV and O stay streamed
+    assert awq.linear_plan(16, 14848, 14848, 128)["x_stage"] == 2
+    assert awq.linear_plan(8, 14848, 59392, 128)["x_stage"] == 2    # fewer than 16 rows
+    assert awq.linear_plan(32, 4096, 6144, 128)["x_stage"] == 2     # narrow
+    assert awq.linear_plan(24, 4096, 28672, 64)["x_stage"] == 2     # G = 64
+    assert awq.linear_silu_mul_plan(32, 4096, 28672, 128)["x_stage"] == 2  # gated: streamed
+    p = awq.linear_plan(5, 384, 40, 128, {"path": 1, "x_stage": 3})
+    assert (p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (3, 2, 8, 1)
+    p = awq.linear_plan(5, 4096, 40, 128, {"path": 1, "x_stage": 3, "tpw": 4, "split_k": 5})
+    assert (p["tpw"], p["split_k"]) == (4, 5)
+    for bad in ({"path": 1, "x_stage": 3, "waves": 4},          # eight waves only
+                {"path": 1, "x_stage": 3, "tpw": 1},            # two or four tiles per wave
+                {"path": 1, "x_stage": 3, "tile": 2},
+                {"path": 2, "x_stage": 3},                      # decode path only
+                {"path": 1, "x_stage": 4}):
+        with pytest.raises(awq.AWQError):
+            awq.linear_plan(16, 4096, 4096, 128, bad)
+    with pytest.raises(awq.AWQError):                           # at most 32 rows
+        awq.linear_plan(33, 4096, 4096, 128, {"path": 1, "x_stage": 3})
+    with pytest.raises(awq.AWQError):                           # whole groups per band
+        awq.linear_plan(16, 4096, 4096, 64, {"path": 1, "x_stage": 3})
+    with pytest.raises(awq.AWQError):                           # not for the gated form
+        awq.linear_silu_mul_plan(16, 4096, 4096, 128, {"path": 1, "x_stage": 3})
 
 
 def test_gated_plans(lib):

@@ -140,7 +140,9 @@ def _exact_case(M, K, N, G, seed=0):
                                   {"path": 2, "tile": 1}, {"path": 2, "tile": 2}, {"path": 2, "tile": 3},
                                   {"path": 2, "tile": 2, "split_k": 3}, {"path": 2, "tile": 3, "split_k": 5},
                                   {"path": 1, "x_stage": 2, "waves": 4, "tpw": 2, "split_k": 3},
-                                  {"path": 1, "x_stage": 2, "waves": 8, "tpw": 4, "split_k": 6}])
+                                  {"path": 1, "x_stage": 2, "waves": 8, "tpw": 4, "split_k": 6},
+                                  {"path": 1, "x_stage": 3, "tpw": 2, "split_k": 1},
+                                  {"path": 1, "x_stage": 3, "tpw": 4, "split_k": 2}])
 def test_exact_case_bitwise(awq, plan):
     M, K, N, G = 9, 768, 72, 128
     log(f"exact M={M} K={K} N={N} plan={plan}")

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <math.h>
+#include <algorithm>
 #include <stdlib.h>
 
 #include "../../include/awq.h"
@@ -84,7 +85,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
                  size_t ws_cap = SIZE_MAX) {
   awq_plan p = {};
   if (in) p = *in;
-  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 2 ||
+  if (p.path < 0 || p.path > 2 || p.split_k < 0 || p.waves < 0 || p.tpw < 0 || p.x_stage < 0 || p.x_stage > 3 ||
       p.tile < 0 || p.tile > 3)
     return AWQ_ERR_PLAN;
   if (gated && N % 32) return AWQ_ERR_SHAPE;
@@ -129,7 +130,7 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       // Fused gate+up: the staged kernel (halves of its waves on the gate
       // and the up tile) for one or two rows, else the streamed one with the
       // two tiles sharing each band's activation loads.
-      if (p.tile) return AWQ_ERR_PLAN;
+      if (p.tile || p.x_stage == 3) return AWQ_ERR_PLAN;
       const int sw = gated_decode_waves(M, K, G, p);
       const bool st = gated_stream_ok(M, p);
       if (sw && (p.x_stage == 1 || M <= 2 || !st)) {
@@ -146,6 +147,32 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
         return AWQ_ERR_PLAN;
       }
       if (out->split > 1 && out->x_stage != 2) return AWQ_ERR_PLAN;
+      out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
+      cap_split(out, M, N, ws_cap, p.split_k == 0);
+      return AWQ_OK;
+    }
+    // Slab variant: eight waves on the same bands, each with its own tpw
+    // column tiles, the activations of two bands at a time staged in LDS
+    // once per workgroup (one activation load per 8 * tpw tiles). Automatic
+    // for 16-32 rows on the largest layers and, above 16 rows, on wide ones
+    // (measured at M = 16: Falcon-180B-shaped up 14848 x 59392 108 -> 83 us,
+    // down 59392 x 14848 103 -> 84 us; its QKV and O within 3% either way,
+    // so left streamed; LLaMA-3-8B gate+up 4096 x 28672 at M = 32: 27.0 ->
+    // 23.6 us, at M = 16 slower, 18.6 -> 19.8). Its workgroups run best as
+    // one round (two per CU with two tiles per wave): K is split until
+    // about 512 workgroups, keeping at least 16 bands per split.
+    const bool slab_auto = !p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 16 && M <= 32 && G % 128 == 0 &&
+                           (NT * KT >= 200000 || (M > 16 && NT >= 1024));
+    if (p.x_stage == 3 || slab_auto) {
+      if (p.tile || M < 1 || M > 32 || G % 128 || (p.waves && p.waves != 8) || (p.tpw && p.tpw != 2 && p.tpw != 4))
+        return AWQ_ERR_PLAN;
+      out->waves = 8;
+      out->tpw = p.tpw ? p.tpw : 2;
+      out->x_stage = 3;
+      const int64_t groups = (NT + 8 * out->tpw - 1) / (8 * out->tpw);
+      const int64_t slots = out->tpw == 2 ? 512 : 256;  // workgroups in one round at this register count
+      const int64_t auto_split = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(slots / groups, KT / 16), 16));
+      out->split = awq::decode_splits((int)K, p.split_k ? p.split_k : (int)auto_split);
       out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
       cap_split(out, M, N, ws_cap, p.split_k == 0);
       return AWQ_OK;
@@ -281,7 +308,8 @@ int run_linear(const uint16_t* x, const uint32_t* qweight, const uint16_t* scale
   awq::LinearArgs a{x, qweight, scales, zeros, y, (int)M, (int)K, (int)N, group};
   const awq::Launch L{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event};
   if (r.path == 1) {
-    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1, gated, r.split, static_cast<float*>(workspace)};
+    const awq::DecodeConfig cfg{r.waves, r.tpw, r.x_stage == 1, gated, r.split, static_cast<float*>(workspace),
+                                r.x_stage == 3};
     return hip_status(awq::launch_decode(a, cfg, L));
   }
   return hip_status(awq::launch_prefill(a, r.tile, r.split, static_cast<float*>(workspace), gated, L));

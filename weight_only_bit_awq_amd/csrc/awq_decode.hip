@@ -557,6 +557,201 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Slab variant (batched rows: every wave of the workgroup on the same bands)
+// ---------------------------------------------------------------------------
+
+// The streamed variant loads each band's activation rows once per wave, so
+// with M rows they cost M/4 times the bytes of a one-tile band. Here the
+// workgroup's waves each own TW adjacent column tiles and walk the same
+// 128-row bands together; the activation rows of kSlabBands bands (a slab)
+// are copied global -> registers -> LDS once per workgroup and every wave
+// reads its MFMA A operand from there, so one activation load serves
+// kSlabWaves * TW tiles. Two slab buffers alternate, one barrier per slab;
+// the next slab's loads are issued before the current slab's products and
+// stored to LDS after them. Weights, scales and zero points come per band
+// into registers, kSlabBands bands ahead. A K split over workgroups works as
+// in the streamed variant (part != nullptr: fp32 sums at
+// part[split][row][column], then the fixed-order reduction kernel). Whole
+// groups per band only (G a multiple of 128).
+constexpr int kSlabWaves = 8;
+constexpr int kSlabBands = 2;
+
+// LDS byte offset of 16-byte chunk `c` of staged activation row `r` (rows of
+// kSlabBands * 16 chunks; the chunk index is XOR-swizzled by the row so that
+// the 16 rows one MFMA operand read touches spread over the banks).
+__device__ __forceinline__ uint32_t slab_off(uint32_t r, uint32_t c) {
+  return (r * (kSlabBands * 16) + (c ^ (r & 15))) * 16;
+}
+
+template <int TW>
+struct SlabBand {
+  u4 wq[TW];
+  uint32_t s[TW];
+  uint32_t zw[TW];
+};
+
+template <int MT, int GPT, int TW>
+__global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint16_t* __restrict__ x,
+                                                                      const u4* __restrict__ qw,
+                                                                      const uint16_t* __restrict__ scales,
+                                                                      const uint32_t* __restrict__ zeros,
+                                                                      uint16_t* __restrict__ y, int M, int K, int N,
+                                                                      int G, int NT, float* __restrict__ part,
+                                                                      int n_groups, int kps) {
+  static_assert(GPT == 0 || GPT == 1, "one group entry per band");
+  static_assert(kSlabBands == 2, "the loop consumes a slab as two bands in the two weight buffers");
+  constexpr int NTH = 64 * kSlabWaves;
+  constexpr int CPR = kSlabBands * 16;  // 16-byte chunks per staged row
+  constexpr int PER = 16 * MT * CPR / NTH;  // staging chunks per thread
+  static_assert(PER * NTH == 16 * MT * CPR, "whole chunks per thread");
+  __shared__ __attribute__((aligned(16))) char slab[2][16 * MT * CPR * 16];
+
+  const int u = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = u / n_groups;
+  const int grp = u - split * n_groups;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 4;
+  const int lcol = lane & 15;
+  const int t0 = (grp * kSlabWaves + w) * TW;  // the wave's first column tile
+  const int groups = K / G;
+  const int tpg = G / 128;
+  const int KT = (K + 127) / 128;
+  const int kt0 = split * kps;
+  const int nb = min(KT, kt0 + kps) - kt0;  // bands of this split, >= 1
+  const int last = kt0 + nb - 1;
+  const int nslab = (nb + kSlabBands - 1) / kSlabBands;
+
+  const rsrc_t rx = make_rsrc(x, (uint32_t)M * (uint32_t)K * 2u);
+  const rsrc_t rs = make_rsrc(scales, (uint32_t)groups * (uint32_t)N * 2u);
+  const rsrc_t rz = make_rsrc(zeros, (uint32_t)groups * (uint32_t)(N / 8) * 4u);
+  const u4* qcol[TW];
+  uint32_t soff[TW], zoff[TW];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) {
+    // tiles past the last one read the last tile's weights (never stored)
+    qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
+    const int col = 16 * (t0 + tt) + lcol;
+    soff[tt] = col < N ? (uint32_t)col * 2u : kOOB;
+    zoff[tt] = col < N ? (uint32_t)(col >> 3) * 4u : kOOB;
+  }
+  const int64_t band = (int64_t)NT * 64;
+  const uint32_t srow = (uint32_t)N * 2u, zrow = (uint32_t)(N / 8) * 4u;
+  auto load_band = [&](SlabBand<TW>& b, int kt) {
+    const uint32_t g = GroupsPerBand<GPT>::group(kt, 0, tpg);
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      b.s[tt] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[tt] + g * srow, 0, 0);
+      b.zw[tt] = __builtin_amdgcn_raw_buffer_load_b32(rz, zoff[tt] + g * zrow, 0, 0);
+      b.wq[tt] = load_weights(qcol[tt] + kt * band);
+    }
+  };
+  // Staging chunk p = i * NTH + tid sits at LDS row p / CPR, position p % CPR,
+  // and holds global chunk (position ^ (row & 15)) of that row of the slab;
+  // rows past M and columns past K read zero.
+  auto load_slab = [&](u4 (&v)[PER], int s) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t p = (uint32_t)(i * NTH) + threadIdx.x;
+      const uint32_t r = p / CPR, pos = p % CPR;
+      const uint32_t kc = 128u * (uint32_t)(kt0 + kSlabBands * s) + 8u * (pos ^ (r & 15u));
+      const bool ok = r < (uint32_t)M && kc < (uint32_t)K;
+      v[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? (r * (uint32_t)K + kc) * 2u : kOOB,
+                                                                            0, 0));
+    }
+  };
+  auto store_slab = [&](const u4 (&v)[PER], int buf) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const uint32_t p = (uint32_t)(i * NTH) + threadIdx.x;
+      *reinterpret_cast<u4*>(slab[buf] + p * 16u) = v[i];
+    }
+  };
+
+  const DecodeConsts kc = decode_consts();
+  f4 acc[TW][MT];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[tt][mt] = f4{0.f, 0.f, 0.f, 0.f};
+
+  // Band bi of the slab in buffer `buf`: A operand from LDS (lane l: row
+  // 16 mt + l % 16, rows 32 j + 8 (l / 16) .. +7 of the band), shared by the
+  // wave's TW tiles.
+  auto consume = [&](const SlabBand<TW>& b, int buf, int bi, float valid) {
+    h8 a[MT][4];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        a[mt][j] = *reinterpret_cast<const h8*>(slab[buf] +
+                                                slab_off((uint32_t)(16 * mt + lcol), (uint32_t)(16 * bi + 4 * j + h)));
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      const ZeroConst zc = zero_const(zero_nibble(b.zw[tt], lcol));
+      f4 accg[MT];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const h8 bw = decode_diff_vk(b.wq[tt][j], zc, kc);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+          accg[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[mt][j], bw, j == 0 ? f4{0.f, 0.f, 0.f, 0.f} : accg[mt],
+                                                            0, 0, 0);
+      }
+      const float sf = valid * scale_of(b.s[tt]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[tt][mt] += sf * accg[mt];
+    }
+  };
+
+  // Prologue: slab 0's loads, the first two bands' weights, slab 0 to LDS.
+  SlabBand<TW> b0, b1;
+  {
+    u4 v[PER];
+    load_slab(v, 0);
+    load_band(b0, kt0);
+    load_band(b1, min(kt0 + 1, last));
+    store_slab(v, 0);
+  }
+  __syncthreads();
+  // Every wave runs the same slabs, so the barriers match; bands past the
+  // split's last one are multiplied by zero (their weights are the last
+  // band's, their activations finite or zero).
+  for (int s = 0; s < nslab; ++s) {
+    const int buf = s & 1;
+    const bool more = s + 1 < nslab;
+    u4 v[PER];
+    if (more) load_slab(v, s + 1);
+    consume(b0, buf, 0, 1.f);
+    load_band(b0, min(kt0 + kSlabBands * s + 2, last));
+    consume(b1, buf, 1, kSlabBands * s + 1 < nb ? 1.f : 0.f);
+    load_band(b1, min(kt0 + kSlabBands * s + 3, last));
+    if (more) store_slab(v, buf ^ 1);
+    __syncthreads();
+  }
+
+  // Each wave holds whole sums (over the split's bands) of its own tiles.
+  // Lane l, register r of row tile mt: row 16 mt + 4 (l / 16) + r, column
+  // 16 (t0 + tt) + l % 16.
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 16 * mt + 4 * h + r;
+        const int col = 16 * (t0 + tt) + lcol;
+        if (row < M && col < N) {
+          if (part)
+            part[((int64_t)split * M + row) * N + col] = acc[tt][mt][r];
+          else
+            y[(int64_t)row * N + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[tt][mt][r]);
+        }
+      }
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -754,6 +949,23 @@ hipError_t launch_stream_g(const LinearArgs& a, int waves, int tw, int splits, f
   return launch_stream_w<MT, 0>(a, waves, tw, splits, ws, L);
 }
 
+template <int MT, int GPT>
+hipError_t launch_slab_t(const LinearArgs& a, int tw, int splits, float* ws, const Launch& L) {
+  const int NT = (a.N + 15) / 16;
+  const int per_group = kSlabWaves * tw;
+  const int groups = (NT + per_group - 1) / per_group;
+  if (tw == 2) return launch_stream_split(decode_slab_kernel<MT, GPT, 2>, groups, kSlabWaves, a, splits, ws, false, L);
+  if (tw == 4) return launch_stream_split(decode_slab_kernel<MT, GPT, 4>, groups, kSlabWaves, a, splits, ws, false, L);
+  return hipErrorInvalidValue;
+}
+
+template <int MT>
+hipError_t launch_slab_g(const LinearArgs& a, int tw, int splits, float* ws, const Launch& L) {
+  if (a.G == 128) return launch_slab_t<MT, 1>(a, tw, splits, ws, L);
+  if (a.G % 128 == 0) return launch_slab_t<MT, 0>(a, tw, splits, ws, L);
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int decode_splits(int K, int splits) { return k_split(K, splits).splits; }
@@ -781,6 +993,12 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
     const StagedSizes z = staged_sizes(a.M, a.K, a.G, cfg.waves, cfg.tpw);
     if (cfg.tpw == 2) return launch_staged_t<2>(a, cfg.waves, z, L);
     return launch_staged_t<1>(a, cfg.waves, z, L);
+  }
+  if (cfg.slab) {
+    if (cfg.waves != kSlabWaves) return hipErrorInvalidValue;
+    if (a.M <= 16) return launch_slab_g<1>(a, cfg.tpw, cfg.splits, cfg.ws, L);
+    if (a.M <= 32) return launch_slab_g<2>(a, cfg.tpw, cfg.splits, cfg.ws, L);
+    return hipErrorInvalidValue;
   }
   if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
   if (a.M <= 32) return launch_stream_g<2>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);

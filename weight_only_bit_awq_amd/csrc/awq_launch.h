@@ -59,6 +59,8 @@ struct DecodeConfig {
   bool gated;  // y[M, N/2] = silu(x W[:, :N/2]) * (x W[:, N/2:]); N % 32 == 0
   int splits;  // streamed: K split over workgroups (fp32 partials in ws, then the fixed-order reduction)
   float* ws;
+  bool slab;   // not staged: activations staged per two-band slab in LDS, shared by four waves that
+               // each own `tpw` column tiles (M <= 32, G a multiple of 128, waves = 4, tpw 2 or 4)
 };
 bool decode_staged_fits(int M, int K, int G, int waves, int tpw);
 // Splits a streamed decode plan actually runs with (whole bands per split,
