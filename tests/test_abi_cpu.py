@@ -252,6 +252,9 @@ def test_slab_plans(lib):
     p = awq.linear_plan(16, 59392, 14848, 128)                  # and down: 58 groups, 464 bands
     assert (p["x_stage"], p["split_k"]) == (3, 8)
     assert awq.linear_workspace_bytes(16, 59392, 14848, 128) == 8 * 16 * 14848 * 4
+    # one round of workgroups: two per CU with one row tile, one with two
+    assert awq.linear_plan(16, 32768, 16384, 128)["split_k"] == 8   # 64 groups x 8 = 512
+    assert awq.linear_plan(32, 32768, 16384, 128)["split_k"] == 4   # 64 groups x 4 = 256
     assert awq.linear_plan(16, 14848, 15872, 128)["x_stage"] == 2   # its QKV and O stay streamed
     assert awq.linear_plan(16, 14848, 14848, 128)["x_stage"] == 2
     assert awq.linear_plan(8, 14848, 59392, 128)["x_stage"] == 2    # fewer than 16 rows

@@ -159,8 +159,8 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     // down 59392 x 14848 103 -> 84 us; its QKV and O within 3% either way,
     // so left streamed; LLaMA-3-8B gate+up 4096 x 28672 at M = 32: 27.0 ->
     // 23.6 us, at M = 16 slower, 18.6 -> 19.8). Its workgroups run best as
-    // one round (two per CU with two tiles per wave): K is split until
-    // about 512 workgroups, keeping at least 16 bands per split.
+    // one round: K is split until about that many workgroups, keeping at
+    // least 16 bands per split.
     const bool slab_auto = !p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 16 && M <= 32 && G % 128 == 0 &&
                            (NT * KT >= 200000 || (M > 16 && NT >= 1024));
     if (p.x_stage == 3 || slab_auto) {
@@ -170,7 +170,9 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
       out->tpw = p.tpw ? p.tpw : 2;
       out->x_stage = 3;
       const int64_t groups = (NT + 8 * out->tpw - 1) / (8 * out->tpw);
-      const int64_t slots = out->tpw == 2 ? 512 : 256;  // workgroups in one round at this register count
+      // workgroups in one round at the kernel's register count: two per CU
+      // with one 16-row tile and two tiles per wave (118 VGPRs), else one
+      const int64_t slots = out->tpw == 2 && M <= 16 ? 512 : 256;
       const int64_t auto_split = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(slots / groups, KT / 16), 16));
       out->split = awq::decode_splits((int)K, p.split_k ? p.split_k : (int)auto_split);
       out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;
