@@ -47,9 +47,12 @@ def _layer(M, K, N, G, seed):
 def test_noalloc_matches_linear_two_calls(awq):
     import torch
     # (M, K, N, G, plan): the first call's partials fill 62.9 MB of the
-    # array; the second is smaller and runs on what the first left behind.
+    # array; each later one is smaller and runs on what the others left behind.
     cases = [(512, 5120, 5120, 128, {"path": 2, "tile": 3, "split_k": 6}),
-             (300, 1024, 1000, 128, {"path": 2, "tile": 2, "split_k": 2})]
+             (300, 1024, 1000, 128, {"path": 2, "tile": 2, "split_k": 2}),
+             # the decode path's slab variant with a K split, on what the
+             # prefill calls left in the array
+             (24, 4096, 2056, 128, {"path": 1, "x_stage": 3, "split_k": 3})]
     for (M, K, N, G, plan) in cases:
         need = awq.linear_workspace_bytes(M, K, N, G, plan)
         assert 0 < need <= SCRATCH_BYTES
