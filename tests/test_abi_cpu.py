@@ -252,9 +252,10 @@ def test_slab_plans(lib):
     p = awq.linear_plan(16, 59392, 14848, 128)                  # and down: 58 groups, 464 bands
     assert (p["x_stage"], p["split_k"]) == (3, 8)
     assert awq.linear_workspace_bytes(16, 59392, 14848, 128) == 8 * 16 * 14848 * 4
-    # one round of workgroups: two per CU with one row tile, one with two
+    # one round of workgroups: two per CU with two tiles per wave, one with four
     assert awq.linear_plan(16, 32768, 16384, 128)["split_k"] == 8   # 64 groups x 8 = 512
-    assert awq.linear_plan(32, 32768, 16384, 128)["split_k"] == 4   # 64 groups x 4 = 256
+    p = awq.linear_plan(16, 32768, 16384, 128, {"path": 1, "x_stage": 3, "tpw": 4})
+    assert p["split_k"] == 8                                        # 32 groups x 8 = 256
     assert awq.linear_plan(16, 14848, 15872, 128)["x_stage"] == 2   # its QKV and O stay streamed
     assert awq.linear_plan(16, 14848, 14848, 128)["x_stage"] == 2
     assert awq.linear_plan(8, 14848, 59392, 128)["x_stage"] == 2    # fewer than 16 rows
@@ -266,7 +267,7 @@ def test_slab_plans(lib):
     p = awq.linear_plan(5, 4096, 40, 128, {"path": 1, "x_stage": 3, "tpw": 4, "split_k": 5})
     assert (p["tpw"], p["split_k"]) == (4, 5)
     for bad in ({"path": 1, "x_stage": 3, "waves": 4},          # eight waves only
-                {"path": 1, "x_stage": 3, "tpw": 1},            # two or four tiles per wave
+                {"path": 1, "x_stage": 3, "tpw": 3},            # one, two or four tiles per wave
                 {"path": 1, "x_stage": 3, "tile": 2},
                 {"path": 2, "x_stage": 3},                      # decode path only
                 {"path": 1, "x_stage": 4}):

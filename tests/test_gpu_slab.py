@@ -2,7 +2,7 @@
 bands, activations staged per two-band slab in LDS) against the fp64 oracle:
 one and two 16-row tiles, an odd number of bands (half-used last slab),
 groups of 128, 256 and 512 rows, partial column tiles and column groups,
-K splits from 1 to 5 with both tile counts per wave; the automatic plans on
+K splits from 1 to 5 with one, two and four tiles per wave; the automatic plans on
 the shapes where they choose it, q == z, and the no-alloc entry point."""
 import numpy as np
 import pytest
@@ -37,7 +37,7 @@ def test_slab_plans(awq, M, K, N, G):
     D = oracle.l1_scale(x, q, z, s, G)
     qw, zw, sd = upload_layer(q, z, s)
     xd = x_dev(x)
-    for tpw in (2, 4):
+    for tpw in (1, 2, 4):
         for split in (0, 1, 2, 3, 5):
             plan = {"path": 1, "x_stage": 3, "tpw": tpw, "split_k": split}
             log(f"  plan {plan} -> {awq.linear_plan(M, K, N, G, plan)}")

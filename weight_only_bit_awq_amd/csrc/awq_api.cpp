@@ -164,15 +164,15 @@ int resolve_plan(int64_t M, int64_t K, int64_t N, int G, const awq_plan* in, Res
     const bool slab_auto = !p.x_stage && !p.tpw && !p.waves && !p.split_k && M >= 16 && M <= 32 && G % 128 == 0 &&
                            (NT * KT >= 200000 || (M > 16 && NT >= 1024));
     if (p.x_stage == 3 || slab_auto) {
-      if (p.tile || M < 1 || M > 32 || G % 128 || (p.waves && p.waves != 8) || (p.tpw && p.tpw != 2 && p.tpw != 4))
+      if (p.tile || M < 1 || M > 32 || G % 128 || (p.waves && p.waves != 8) || p.tpw == 3)
         return AWQ_ERR_PLAN;
       out->waves = 8;
       out->tpw = p.tpw ? p.tpw : 2;
       out->x_stage = 3;
       const int64_t groups = (NT + 8 * out->tpw - 1) / (8 * out->tpw);
       // workgroups in one round at the kernel's register count: two per CU
-      // with one 16-row tile and two tiles per wave (118 VGPRs), else one
-      const int64_t slots = out->tpw == 2 && M <= 16 ? 512 : 256;
+      // with one or two tiles per wave (at most 121 VGPRs), one with four
+      const int64_t slots = out->tpw <= 2 ? 512 : 256;
       const int64_t auto_split = std::max<int64_t>(1, std::min<int64_t>(std::min<int64_t>(slots / groups, KT / 16), 16));
       out->split = awq::decode_splits((int)K, p.split_k ? p.split_k : (int)auto_split);
       out->ws_bytes = out->split > 1 ? (size_t)out->split * (size_t)M * (size_t)N * 4 : 0;

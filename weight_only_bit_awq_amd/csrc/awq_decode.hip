@@ -954,6 +954,7 @@ hipError_t launch_slab_t(const LinearArgs& a, int tw, int splits, float* ws, con
   const int NT = (a.N + 15) / 16;
   const int per_group = kSlabWaves * tw;
   const int groups = (NT + per_group - 1) / per_group;
+  if (tw == 1) return launch_stream_split(decode_slab_kernel<MT, GPT, 1>, groups, kSlabWaves, a, splits, ws, false, L);
   if (tw == 2) return launch_stream_split(decode_slab_kernel<MT, GPT, 2>, groups, kSlabWaves, a, splits, ws, false, L);
   if (tw == 4) return launch_stream_split(decode_slab_kernel<MT, GPT, 4>, groups, kSlabWaves, a, splits, ws, false, L);
   return hipErrorInvalidValue;
