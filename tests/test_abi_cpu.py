@@ -261,7 +261,9 @@ def test_slab_plans(lib):
     assert awq.linear_plan(8, 14848, 59392, 128)["x_stage"] == 2    # fewer than 16 rows
     assert awq.linear_plan(32, 4096, 6144, 128)["x_stage"] == 2     # narrow
     assert awq.linear_plan(24, 4096, 28672, 64)["x_stage"] == 2     # G = 64
-    assert awq.linear_silu_mul_plan(32, 4096, 28672, 128)["x_stage"] == 2  # gated: streamed
+    p = awq.linear_silu_mul_plan(32, 4096, 28672, 128)         # gated: the same rule
+    assert (p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (3, 2, 8, 2)
+    assert awq.linear_silu_mul_plan(16, 4096, 28672, 128)["x_stage"] == 2
     p = awq.linear_plan(5, 384, 40, 128, {"path": 1, "x_stage": 3})
     assert (p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (3, 2, 8, 1)
     p = awq.linear_plan(5, 4096, 40, 128, {"path": 1, "x_stage": 3, "tpw": 4, "split_k": 5})
@@ -277,8 +279,8 @@ def test_slab_plans(lib):
         awq.linear_plan(33, 4096, 4096, 128, {"path": 1, "x_stage": 3})
     with pytest.raises(awq.AWQError):                           # whole groups per band
         awq.linear_plan(16, 4096, 4096, 64, {"path": 1, "x_stage": 3})
-    with pytest.raises(awq.AWQError):                           # not for the gated form
-        awq.linear_silu_mul_plan(16, 4096, 4096, 128, {"path": 1, "x_stage": 3})
+    with pytest.raises(awq.AWQError):                           # gated: two or four tiles per wave
+        awq.linear_silu_mul_plan(16, 4096, 4096, 128, {"path": 1, "x_stage": 3, "tpw": 1})
 
 
 def test_gated_plans(lib):
@@ -291,9 +293,10 @@ def test_gated_plans(lib):
     # paired; above 32 rows: the GEMM
     p = awq.linear_silu_mul_plan(2, 4096, 28672, 128)
     assert (p["path"], p["x_stage"], p["tpw"]) == (1, 1, 1)
-    for M, tw in ((4, 4), (8, 4), (16, 4), (32, 4)):
+    for M, tw in ((4, 4), (8, 4), (16, 4)):
         p = awq.linear_silu_mul_plan(M, 4096, 28672, 128)
         assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, tw, 4), (M, p)
+    assert awq.linear_silu_mul_plan(32, 4096, 28672, 128)["x_stage"] == 3   # slab above 16 rows
     with pytest.raises(awq.AWQError):                            # two tile pairs need an even number per half
         awq.linear_silu_mul_plan(8, 1024, 96, 128, {"path": 1, "x_stage": 2, "tpw": 4})
     assert awq.linear_silu_mul_plan(40, 4096, 28672, 128)["path"] == 2

@@ -1,7 +1,8 @@
 """GPU parity of the gated epilogue awq_linear_silu_mul (y = silu(gate) * up
 on a fused gate+up layer) against the fp64 oracle, on the fused decode
-kernel and on the prefill path (split and unsplit), with the derived error
-scale 1.1 |u| D_gate + |silu(g)| D_up + |y| and the same 2e-3 budget."""
+kernel (staged, streamed and slab variants) and on the prefill path (split
+and unsplit), with the derived error scale 1.1 |u| D_gate + |silu(g)| D_up
++ |y| and the same 2e-3 budget."""
 import numpy as np
 import pytest
 
@@ -52,7 +53,12 @@ def sampled(q, z, s, cols):
     # the streamed decode kernel with K split over workgroups
     (16, 4096, 2048, 128, {"path": 1, "x_stage": 2, "tpw": 4, "split_k": 4}),
     (32, 1216, 128, 64, {"path": 1, "tpw": 2, "waves": 8, "split_k": 3}),
-    (5, 3200, 96, 32, {"path": 1, "x_stage": 2, "tpw": 2, "split_k": 16})])
+    (5, 3200, 96, 32, {"path": 1, "x_stage": 2, "tpw": 2, "split_k": 16}),
+    # the slab variant: gate and up tiles of each wave, with and without a K split
+    (16, 1024, 2048, 128, {"path": 1, "x_stage": 3}), (32, 1280, 544, 128, {"path": 1, "x_stage": 3, "split_k": 3}),
+    (5, 512, 96, 256, {"path": 1, "x_stage": 3, "tpw": 4}),
+    (17, 2048, 4128, 128, {"path": 1, "x_stage": 3, "tpw": 4, "split_k": 2}),
+    (24, 640, 160, 128, {"path": 1, "x_stage": 3, "split_k": 5})])
 def test_gated_matches_oracle(awq, M, K, N, G, plan):
     log(f"gated M={M} K={K} N={N} G={G} plan={plan}")
     q, z, s = synth.layer(K, N, G, seed=M + K + N)

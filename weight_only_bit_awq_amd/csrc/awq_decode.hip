@@ -574,7 +574,11 @@ __global__ __launch_bounds__(64 * WAVES) void decode_stream_kernel(const uint16_
 // into registers, kSlabBands bands ahead. A K split over workgroups works as
 // in the streamed variant (part != nullptr: fp32 sums at
 // part[split][row][column], then the fixed-order reduction kernel). Whole
-// groups per band only (G a multiple of 128).
+// groups per band only (G a multiple of 128). GATED (TW = 2 or 4): each wave
+// holds TW/2 adjacent tiles of the gate half and the same tiles of the up
+// half and stores y[m, n] = silu(gate) * up ([M, N/2]); with a K split the
+// gate and up sums go to their global columns and the reduction applies the
+// epilogue.
 constexpr int kSlabWaves = 8;
 constexpr int kSlabBands = 2;
 
@@ -592,7 +596,7 @@ struct SlabBand {
   uint32_t zw[TW];
 };
 
-template <int MT, int GPT, int TW>
+template <int MT, int GPT, int TW, bool GATED = false>
 __global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint16_t* __restrict__ x,
                                                                       const u4* __restrict__ qw,
                                                                       const uint16_t* __restrict__ scales,
@@ -601,6 +605,8 @@ __global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint
                                                                       int G, int NT, float* __restrict__ part,
                                                                       int n_groups, int kps) {
   static_assert(GPT == 0 || GPT == 1, "one group entry per band");
+  static_assert(!GATED || TW == 2 || TW == 4, "gated: gate tiles and as many up tiles");
+  constexpr int TH = GATED ? TW / 2 : TW;  // gate tiles (gated) or tiles per wave
   static_assert(kSlabBands == 2, "the loop consumes a slab as two bands in the two weight buffers");
   constexpr int NTH = 64 * kSlabWaves;
   constexpr int CPR = kSlabBands * 16;  // 16-byte chunks per staged row
@@ -615,7 +621,12 @@ __global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int h = lane >> 4;
   const int lcol = lane & 15;
-  const int t0 = (grp * kSlabWaves + w) * TW;  // the wave's first column tile
+  const int t0 = (grp * kSlabWaves + w) * TH;  // the wave's first (gate) column tile
+  const int NO = N / 2;                         // gated: output columns
+  // column tile of the wave's tile tt: the up tiles lie NT/2 after the gate tiles
+  auto tile_of = [&](int tt) { return GATED && tt >= TH ? NT / 2 + t0 + (tt - TH) : t0 + tt; };
+  // the tile's column exists (gated: its output column)
+  auto col_ok = [&](int tt) { return GATED ? 16 * (t0 + tt % TH) + lcol < NO : 16 * (t0 + tt) + lcol < N; };
   const int groups = K / G;
   const int tpg = G / 128;
   const int KT = (K + 127) / 128;
@@ -632,10 +643,10 @@ __global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint
 #pragma unroll
   for (int tt = 0; tt < TW; ++tt) {
     // tiles past the last one read the last tile's weights (never stored)
-    qcol[tt] = qw + (int64_t)min(t0 + tt, NT - 1) * 64 + lane;
-    const int col = 16 * (t0 + tt) + lcol;
-    soff[tt] = col < N ? (uint32_t)col * 2u : kOOB;
-    zoff[tt] = col < N ? (uint32_t)(col >> 3) * 4u : kOOB;
+    qcol[tt] = qw + (int64_t)min(tile_of(tt), NT - 1) * 64 + lane;
+    const int col = 16 * tile_of(tt) + lcol;
+    soff[tt] = col_ok(tt) ? (uint32_t)col * 2u : kOOB;
+    zoff[tt] = col_ok(tt) ? (uint32_t)(col >> 3) * 4u : kOOB;
   }
   const int64_t band = (int64_t)NT * 64;
   const uint32_t srow = (uint32_t)N * 2u, zrow = (uint32_t)(N / 8) * 4u;
@@ -734,7 +745,29 @@ __global__ __launch_bounds__(64 * kSlabWaves) void decode_slab_kernel(const uint
 
   // Each wave holds whole sums (over the split's bands) of its own tiles.
   // Lane l, register r of row tile mt: row 16 mt + 4 (l / 16) + r, column
-  // 16 (t0 + tt) + l % 16.
+  // 16 (t0 + tt) + l % 16 (gated: output column; the up sums in tile tt + TH).
+  if constexpr (GATED) {
+#pragma unroll
+    for (int pt = 0; pt < TH; ++pt)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * mt + 4 * h + r;
+          const int oc = 16 * (t0 + pt) + lcol;
+          const float g = acc[pt][mt][r], up = acc[TH + pt][mt][r];
+          if (row < M && oc < NO) {
+            if (part) {
+              float* pr = part + ((int64_t)split * M + row) * N;
+              pr[oc] = g;
+              pr[NO + oc] = up;
+            } else {
+              y[(int64_t)row * NO + oc] = __builtin_bit_cast(uint16_t, (_Float16)(g / (1.f + expf(-g)) * up));
+            }
+          }
+        }
+    return;
+  }
 #pragma unroll
   for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
@@ -950,8 +983,19 @@ hipError_t launch_stream_g(const LinearArgs& a, int waves, int tw, int splits, f
 }
 
 template <int MT, int GPT>
-hipError_t launch_slab_t(const LinearArgs& a, int tw, int splits, float* ws, const Launch& L) {
+hipError_t launch_slab_t(const LinearArgs& a, int tw, int splits, float* ws, bool gated, const Launch& L) {
   const int NT = (a.N + 15) / 16;
+  if (gated) {
+    // N % 32 == 0: each half is whole tiles
+    if (a.N % 32) return hipErrorInvalidValue;
+    const int per_group = kSlabWaves * (tw / 2);
+    const int groups = (NT / 2 + per_group - 1) / per_group;
+    if (tw == 2)
+      return launch_stream_split(decode_slab_kernel<MT, GPT, 2, true>, groups, kSlabWaves, a, splits, ws, true, L);
+    if (tw == 4)
+      return launch_stream_split(decode_slab_kernel<MT, GPT, 4, true>, groups, kSlabWaves, a, splits, ws, true, L);
+    return hipErrorInvalidValue;
+  }
   const int per_group = kSlabWaves * tw;
   const int groups = (NT + per_group - 1) / per_group;
   if (tw == 1) return launch_stream_split(decode_slab_kernel<MT, GPT, 1>, groups, kSlabWaves, a, splits, ws, false, L);
@@ -961,9 +1005,9 @@ hipError_t launch_slab_t(const LinearArgs& a, int tw, int splits, float* ws, con
 }
 
 template <int MT>
-hipError_t launch_slab_g(const LinearArgs& a, int tw, int splits, float* ws, const Launch& L) {
-  if (a.G == 128) return launch_slab_t<MT, 1>(a, tw, splits, ws, L);
-  if (a.G % 128 == 0) return launch_slab_t<MT, 0>(a, tw, splits, ws, L);
+hipError_t launch_slab_g(const LinearArgs& a, int tw, int splits, float* ws, bool gated, const Launch& L) {
+  if (a.G == 128) return launch_slab_t<MT, 1>(a, tw, splits, ws, gated, L);
+  if (a.G % 128 == 0) return launch_slab_t<MT, 0>(a, tw, splits, ws, gated, L);
   return hipErrorInvalidValue;
 }
 
@@ -981,6 +1025,12 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
   if (cfg.gated) {
     // gate and up tiles paired in one workgroup
     if (a.N % 32) return hipErrorInvalidValue;
+    if (cfg.slab) {
+      if (cfg.waves != kSlabWaves) return hipErrorInvalidValue;
+      if (a.M <= 16) return launch_slab_g<1>(a, cfg.tpw, cfg.splits, cfg.ws, true, L);
+      if (a.M <= 32) return launch_slab_g<2>(a, cfg.tpw, cfg.splits, cfg.ws, true, L);
+      return hipErrorInvalidValue;
+    }
     if (!cfg.staged) {
       if (a.M <= 16) return launch_stream_gated_g<1>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
       if (a.M <= 32) return launch_stream_gated_g<2>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
@@ -997,8 +1047,8 @@ hipError_t launch_decode(const LinearArgs& a, const DecodeConfig& cfg, const Lau
   }
   if (cfg.slab) {
     if (cfg.waves != kSlabWaves) return hipErrorInvalidValue;
-    if (a.M <= 16) return launch_slab_g<1>(a, cfg.tpw, cfg.splits, cfg.ws, L);
-    if (a.M <= 32) return launch_slab_g<2>(a, cfg.tpw, cfg.splits, cfg.ws, L);
+    if (a.M <= 16) return launch_slab_g<1>(a, cfg.tpw, cfg.splits, cfg.ws, false, L);
+    if (a.M <= 32) return launch_slab_g<2>(a, cfg.tpw, cfg.splits, cfg.ws, false, L);
     return hipErrorInvalidValue;
   }
   if (a.M <= 16) return launch_stream_g<1>(a, cfg.waves, cfg.tpw, cfg.splits, cfg.ws, L);
