@@ -367,11 +367,15 @@ def gated_times(awq, lib, torch, hip, K, N, G, M, dev, copies, reps):
 def decode_sweep(awq, lib, torch, hip, wl, dev, seed, layers=8, reps=3):
     """Batched decode on the LLaMA-3-8B-shaped layers: for each M, the four
     shapes' kernels (events at their own start and end) over `layers` copies
-    of each, cold weights; weight GB/s and TFLOP/s of one layer's four calls."""
+    of each, cold weights; weight GB/s and TFLOP/s of one layer's four calls.
+    Also the same `layers` layers captured in one HIP graph and replayed
+    (graph_*): a plan of two launches (K split, then the reduction) costs
+    less between its kernels there than eagerly."""
     out = {}
     for M in wl.Ms:
         stack, _ = build_stack(awq, torch, wl, M, dev, seed, layers=layers)
         t = per_kernel_times(lib, torch, hip, stack, reps)
+        _, graph_ms = time_stack_graph(lib, torch, stack, 20, 3)
         layer_ms = sum(sum(v) / len(v) for v in t.values())
         wb = sum(weight_set_bytes(sh.K, sh.N, wl.G) for sh in wl.shapes)
         fl = sum(2.0 * M * sh.K * sh.N for sh in wl.shapes)
@@ -382,8 +386,11 @@ def decode_sweep(awq, lib, torch, hip, wl, dev, seed, layers=8, reps=3):
                                   "weight_GBps": round(weight_set_bytes(sh.K, sh.N, wl.G) / us / 1e3, 1),
                                   "plan": awq.linear_plan(M, sh.K, sh.N, wl.G),
                                   "traffic": traffic_set_entry(f"{wl.name}/{sh.name}@M={M}")}
+        glayer_ms = graph_ms / layers
         out[f"M={M}"] = {"layer_us": round(layer_ms * 1e3, 2), "weight_GBps": round(wb / (layer_ms / 1e3) / 1e9, 1),
-                         "TFLOPs": round(fl / (layer_ms / 1e3) / 1e12, 2), "per_shape": per_shape}
+                         "TFLOPs": round(fl / (layer_ms / 1e3) / 1e12, 2),
+                         "graph_layer_us": round(glayer_ms * 1e3, 2),
+                         "graph_weight_GBps": round(wb / (glayer_ms / 1e3) / 1e9, 1), "per_shape": per_shape}
         del stack
         torch.cuda.empty_cache()
     return out
@@ -1250,7 +1257,8 @@ def main():
         ws3 = synth.LLAMA3_8B_SWEEP
         sweep = {"workload": ws3.name, "group": ws3.G, "per_M": decode_sweep(awq, lib, torch, hip, ws3, dev,
                                                                              args.seed + 3)}
-        eprint("[bench] decode sweep: " + ", ".join(f"{k} {v['layer_us']}us {v['weight_GBps']}GB/s"
+        eprint("[bench] decode sweep: " + ", ".join(f"{k} {v['layer_us']}us {v['weight_GBps']}GB/s "
+                                                     f"(graph {v['graph_layer_us']}us)"
                                                     for k, v in sweep["per_M"].items()))
 
     # Gated epilogue (silu(gate) * up) on the fused gate+up layer.
