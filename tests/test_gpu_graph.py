@@ -28,6 +28,10 @@ def test_graph_replays_match_eager(awq):
         (300, 1024, 256, 128, None, False),
         (1, 1024, 256, 64, None, True),
         (130, 2304, 160, 256, {"path": 2, "split_k": 3}, True),
+        # the decode path's slab variant, split (reduction kernel) and not, plain and gated
+        (24, 2048, 1024, 128, {"path": 1, "x_stage": 3, "split_k": 3}, False),
+        (16, 1024, 512, 128, {"path": 1, "x_stage": 3, "tpw": 1}, False),
+        (32, 1280, 544, 128, {"path": 1, "x_stage": 3, "split_k": 2}, True),
     ]
     layers = []
     for i, (M, K, N, G, plan, gated) in enumerate(cases):
