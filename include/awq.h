@@ -246,8 +246,9 @@ int awq_linear_noalloc(const uint16_t* x, const uint32_t* qweight, const uint16_
  * (passed as void*, either may be NULL): `start_event` at the start of the
  * call's first kernel and `stop_event` at the end of its last kernel
  * (hipExtLaunchKernelGGL), so that hipEventElapsedTime gives the call's own
- * kernel time. A call is one kernel, or two for a prefill plan with
- * split_k > 1 (the GEMM, then the fixed-order reduction of its partials).
+ * kernel time. A call is one kernel, or two for a plan with split_k > 1
+ * (the GEMM or decode kernel, then the fixed-order reduction of its
+ * partials).
  * For measurement only: not for use under stream capture.
  */
 int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
@@ -266,10 +267,12 @@ int awq_linear_timed(const uint16_t* x, const uint32_t* qweight, const uint16_t*
  * y is [M, N/2], 8-byte aligned. N % 32 == 0. TinyChat ("Speed Benchmarks",
  * LLaMA-family models) fuses the small operators around its W4A16 kernels;
  * here the activation runs in the decode kernel's epilogue (one launch, no
- * [M, N] intermediate), or, on the prefill path, where the fp32 partial sums
- * are added (the workspace then holds split_k * M * N fp32 values even for
- * split_k = 1). Plans, workspace and errors as for awq_linear; the decode
- * path needs M <= 16 and the LDS-staged variant with paired tiles.
+ * [M, N] intermediate), or, with a K split, where the fp32 partial sums are
+ * added (the gate and up sums at their own columns of the split_k * M * N
+ * workspace). Plans, workspace and errors as for awq_linear; on the decode
+ * path (M <= 32) the staged variant pairs the gate and up tiles in one
+ * workgroup (M <= 16), the streamed and slab variants in one wave (tpw 2 or
+ * 4: half gate, half up tiles).
  */
 int awq_linear_silu_mul(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                         const uint32_t* zeros, int64_t M, int64_t K, int64_t N, int group,
