@@ -222,8 +222,8 @@ def test_batched_decode_plans(lib):
     assert awq.linear_plan(4, 4096, 4096, 128)["x_stage"] == 1  # 4 rows: staged
     p = awq.linear_plan(16, 4096, 28672, 128)                   # 1792 tiles: four per workgroup
     assert (p["path"], p["x_stage"], p["tpw"], p["waves"]) == (1, 2, 4, 4)
-    p = awq.linear_plan(32, 4096, 28672, 128)                   # above 16 rows, wide: slab, K in two
-    assert (p["path"], p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (1, 3, 2, 8, 2)
+    p = awq.linear_plan(32, 4096, 28672, 128)                   # above 16 rows, wide: slab, one tile per wave
+    assert (p["path"], p["x_stage"], p["tpw"], p["waves"], p["split_k"]) == (1, 3, 1, 8, 1)
     p = awq.linear_plan(32, 4096, 28672, 32)                    # 32-row groups at 32 rows: two
     assert p["tpw"] == 2
     p = awq.linear_plan(4, 14336, 4096, 128)                    # 256 tiles: staged, sixteen waves
@@ -254,6 +254,8 @@ def test_slab_plans(lib):
     assert awq.linear_workspace_bytes(16, 59392, 14848, 128) == 8 * 16 * 14848 * 4
     # one round of workgroups: two per CU with two tiles per wave, one with four
     assert awq.linear_plan(16, 32768, 16384, 128)["split_k"] == 8   # 64 groups x 8 = 512
+    p = awq.linear_plan(32, 32768, 16384, 128)                      # above 16 rows: one tile, one per CU
+    assert (p["tpw"], p["split_k"]) == (1, 2)                       # 128 groups x 2 = 256
     p = awq.linear_plan(16, 32768, 16384, 128, {"path": 1, "x_stage": 3, "tpw": 4})
     assert p["split_k"] == 8                                        # 32 groups x 8 = 256
     assert awq.linear_plan(16, 14848, 15872, 128)["x_stage"] == 2   # its QKV and O stay streamed
