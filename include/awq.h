@@ -158,7 +158,8 @@ int awq_quantize(const uint16_t* w, int64_t K, int64_t N, int group, uint32_t* q
  *   tpw:     decode path: 16-column tiles per workgroup: 1 or 2 with staged
  *            activations; 1, 2 or 4 with streamed activations (M <= 32, 4 or
  *            8 waves), where each wave's activation loads serve all of them;
- *            slab variant: tiles per wave, 1, 2 or 4 (automatic: 2).
+ *            slab variant: tiles per wave, 1, 2 or 4 (automatic: 2 up to 16
+ *            rows, 1 above; gated: 2 or 4, half gate and half up).
  *   x_stage: decode path: 1 = activations and the (scale, zero point) words
  *            of the workgroup's columns staged in LDS once per workgroup
  *            (needs M <= 16 and the data to fit in 160 KiB), 2 = activations,
